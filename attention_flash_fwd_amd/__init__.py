@@ -1,0 +1,135 @@
+"""Exact FlashAttention-style attention forward for AMD MI355X (gfx950).
+
+Thin binding over libattn.so (C ABI in include/attn.h): argument marshalling
+only.  torch supplies device memory and the current stream; every step of the
+computation runs in the library's HIP kernels.  There is no CPU fallback: a
+missing library or a non-GPU tensor raises.
+
+    o, lse = prefill(q, k, v, causal=True)             # q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D]
+    o, lse = decode_paged(q, k_cache, v_cache, block_table, ctx_lens, num_splits=0)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+from . import _lib
+from ._lib import AttnError, MAX_SPLITS  # noqa: F401
+
+__all__ = ["prefill", "decode_paged", "decode_num_splits", "decode_workspace_bytes",
+           "decode_workspace", "AttnError", "library_path"]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _stream_handle(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return _lib.ATTN_BF16
+    if t.dtype == torch.float32:
+        return _lib.ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("attention_flash_fwd_amd runs on the GPU only; got a CPU tensor")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else 0)
+
+
+def prefill(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse_out=None,
+            return_lse: bool = True):
+    """Exact attention forward.  q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D], bf16 or fp32.
+
+    Returns (o [B,Sq,Hq,D] in q's dtype, lse [B,Hq,Sq] fp32 or None)."""
+    import torch
+    lib = _lib.load()
+    _need_gpu(q, k, v, out, lse_out)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q [B,Sq,Hq,D] and k, v [B,Sk,Hkv,D]")
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v disagree in batch, head_dim or dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = out if out is not None else torch.empty_like(q)
+    lse = lse_out
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    st = lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                          B, Sq, Sk, Hq, Hkv, D, int(bool(causal)), float(scale),
+                          _dtype_code(q), _stream_handle(q))
+    if st != _lib.ATTN_OK:
+        raise AttnError(st, "attn_prefill")
+    return o, lse
+
+
+def decode_num_splits(batch, n_kv_heads, max_blocks_per_seq, block_size=16, num_splits=0) -> int:
+    return int(_lib.load().attn_decode_num_splits(batch, n_kv_heads, max_blocks_per_seq,
+                                                  block_size, num_splits))
+
+
+def decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, max_blocks_per_seq,
+                           block_size=16, num_splits=0) -> int:
+    return int(_lib.load().attn_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
+                                                       max_blocks_per_seq, block_size, num_splits))
+
+
+def decode_workspace(q, k_cache, block_table, num_splits=0):
+    """Allocate a workspace tensor sized for these decode arguments."""
+    import torch
+    B, Hq, D = q.shape
+    nbytes = decode_workspace_bytes(B, Hq, k_cache.shape[2], D, block_table.shape[1],
+                                    k_cache.shape[1], num_splits)
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+
+
+def decode_paged(q, k_cache, v_cache, block_table, ctx_lens, num_splits: int = 0,
+                 scale: float | None = None, out=None, lse_out=None, workspace=None,
+                 return_lse: bool = True):
+    """One query token per sequence over a paged bf16 KV cache.
+
+    q [B,Hq,D]; k_cache/v_cache [num_blocks,16,Hkv,D]; block_table [B,max_blocks]
+    int32; ctx_lens [B] int32.  Returns (o [B,Hq,D] bf16, lse [B,Hq] fp32 or None)."""
+    import torch
+    lib = _lib.load()
+    _need_gpu(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out, workspace)
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise TypeError("decode_paged takes bf16 q and caches")
+    if block_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
+        raise TypeError("block_table and ctx_lens must be int32")
+    B, Hq, D = q.shape
+    nblocks, bs, Hkv, Dk = k_cache.shape
+    if Dk != D or v_cache.shape != k_cache.shape or block_table.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("inconsistent decode shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    max_blocks = block_table.shape[1]
+    if workspace is None:
+        workspace = decode_workspace(q, k_cache, block_table, num_splits)
+    o = out if out is not None else torch.empty_like(q)
+    lse = lse_out
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = lib.attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                               _ptr(ctx_lens), _ptr(o), _ptr(lse),
+                               B, Hq, Hkv, D, nblocks, bs, max_blocks, int(num_splits),
+                               float(scale), _ptr(workspace), workspace.numel(),
+                               _stream_handle(q))
+    if st != _lib.ATTN_OK:
+        raise AttnError(st, "attn_decode_paged")
+    return o, lse

@@ -1,0 +1,184 @@
+// attn_api.cpp -- the C ABI of libattn.so (declared in include/attn.h).
+//
+// Every argument is checked on the host before any HIP call; a rejected call
+// enqueues nothing and touches no output.  Accepted calls enqueue their
+// kernels on the caller's stream and return without synchronising.
+#include "../../include/attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr long long kMaxElems = 1LL << 31;   // per-tensor element limit of the prefill path
+constexpr int kBlockSize = 16;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+attn_status_t check_prefill(const void *q, const void *k, const void *v, const void *o,
+                            const float *lse, int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                            attn_dtype_t dtype)
+{
+    if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+    if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return ATTN_ERR_SHAPE;
+    if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)B * Sq * Hq * D >= kMaxElems || (long long)B * Sk * Hkv * D >= kMaxElems)
+        return ATTN_ERR_SHAPE;
+    if (B == 0 || Sq == 0) return ATTN_OK;
+    if (q == nullptr || o == nullptr) return ATTN_ERR_NULL;
+    if (Sk > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k, 16) || !aligned(v, 16)) return ATTN_ERR_ALIGN;
+    if (lse != nullptr && !aligned(lse, 4)) return ATTN_ERR_ALIGN;
+    return ATTN_OK;
+}
+
+// Chunks per sequence for decode: explicit, or enough to put several
+// workgroups on each of the 256 compute units with chunks of >= 256 tokens.
+int resolve_splits(int batch, int n_kv_heads, int max_blocks, int block_size, int num_splits)
+{
+    if (num_splits >= 1) return num_splits <= ATTN_MAX_SPLITS ? num_splits : 0;
+    const long long max_tokens = (long long)max_blocks * block_size;
+    const long long units = (long long)batch * n_kv_heads;
+    if (units <= 0) return 1;
+    const long long target_wg = 2048;
+    long long s = (target_wg + units - 1) / units;
+    long long cap = (max_tokens + 255) / 256;
+    if (cap < 1) cap = 1;
+    if (s > cap) s = cap;
+    if (s > ATTN_MAX_SPLITS) s = ATTN_MAX_SPLITS;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t part_o_bytes(int B, int Hq, int D, int S) { return align_up((size_t)B * Hq * S * D * sizeof(float), 256); }
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char *attn_status_string(attn_status_t s)
+{
+    switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "null pointer";
+    case ATTN_ERR_ALIGN: return "misaligned pointer";
+    case ATTN_ERR_SHAPE: return "invalid shape";
+    case ATTN_ERR_DTYPE: return "invalid dtype";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o, float *lse,
+                           int batch, int seqlen_q, int seqlen_k, int n_q_heads, int n_kv_heads,
+                           int head_dim, int causal, float scale, attn_dtype_t dtype,
+                           attn_stream_t stream)
+{
+    attn_status_t st = check_prefill(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_q_heads,
+                                     n_kv_heads, head_dim, dtype);
+    if (st != ATTN_OK || batch == 0 || seqlen_q == 0) return st;
+
+    attn::PrefillArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.B = batch;
+    a.Sq = seqlen_q;
+    a.Sk = seqlen_k;
+    a.Hq = n_q_heads;
+    a.Hkv = n_kv_heads;
+    a.scale_log2 = scale * kLog2e;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = dtype == ATTN_BF16 ? attn::launch_prefill_bf16(a, head_dim, causal != 0, s)
+                                      : attn::launch_prefill_f32(a, head_dim, causal != 0, s);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_decode_num_splits(int batch, int n_kv_heads, int max_blocks_per_seq, int block_size,
+                           int num_splits)
+{
+    if (batch < 0 || n_kv_heads <= 0 || max_blocks_per_seq < 0 || block_size <= 0) return 0;
+    return resolve_splits(batch, n_kv_heads, max_blocks_per_seq, block_size, num_splits);
+}
+
+size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                   int max_blocks_per_seq, int block_size, int num_splits)
+{
+    if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0) return 0;
+    const int S = attn_decode_num_splits(batch, n_kv_heads, max_blocks_per_seq, block_size, num_splits);
+    if (S <= 0) return 0;
+    return part_o_bytes(batch, n_q_heads, head_dim, S) +
+           align_up((size_t)batch * n_q_heads * S * sizeof(float), 256);
+}
+
+attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *block_table, const int32_t *ctx_lens,
+                                void *o, float *lse,
+                                int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                int num_blocks, int block_size, int max_blocks_per_seq,
+                                int num_splits, float scale,
+                                void *workspace, size_t workspace_bytes,
+                                attn_stream_t stream)
+{
+    if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || num_blocks < 0 ||
+        max_blocks_per_seq < 0 || block_size <= 0)
+        return ATTN_ERR_SHAPE;
+    if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+    if (block_size != kBlockSize) return ATTN_ERR_UNSUPPORTED;
+    if (n_q_heads / n_kv_heads > 16) return ATTN_ERR_UNSUPPORTED;
+    if (num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)max_blocks_per_seq * block_size >= kMaxElems) return ATTN_ERR_SHAPE;
+    if ((long long)batch * n_q_heads * head_dim >= kMaxElems) return ATTN_ERR_SHAPE;
+    if (batch == 0) return ATTN_OK;
+    if (q == nullptr || o == nullptr || block_table == nullptr || ctx_lens == nullptr)
+        return ATTN_ERR_NULL;
+    if (num_blocks > 0 && (k_cache == nullptr || v_cache == nullptr)) return ATTN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+        return ATTN_ERR_ALIGN;
+    if (!aligned(block_table, 4) || !aligned(ctx_lens, 4)) return ATTN_ERR_ALIGN;
+    if (lse != nullptr && !aligned(lse, 4)) return ATTN_ERR_ALIGN;
+
+    const int S = resolve_splits(batch, n_kv_heads, max_blocks_per_seq, block_size, num_splits);
+    const size_t need = attn_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
+                                                    max_blocks_per_seq, block_size, num_splits);
+    if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+
+    attn::DecodeArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k_cache = static_cast<const uint16_t *>(k_cache);
+    a.v_cache = static_cast<const uint16_t *>(v_cache);
+    a.block_table = block_table;
+    a.ctx_lens = ctx_lens;
+    a.part_o = static_cast<float *>(workspace);
+    a.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                           part_o_bytes(batch, n_q_heads, head_dim, S));
+    a.o = static_cast<uint16_t *>(o);
+    a.lse = lse;
+    a.B = batch;
+    a.Hq = n_q_heads;
+    a.Hkv = n_kv_heads;
+    a.num_blocks = num_blocks;
+    a.max_blocks = max_blocks_per_seq;
+    a.splits = S;
+    a.scale_log2 = scale * kLog2e;
+    hipError_t e = attn::launch_decode(a, head_dim, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"

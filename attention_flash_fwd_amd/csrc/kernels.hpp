@@ -1,0 +1,36 @@
+// kernels.hpp -- argument blocks and launchers of the device kernels.
+// Host code (attn_api.cpp) validates every argument before calling these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct PrefillArgs {
+    const void *q, *k, *v;    // [B,Sq,Hq,D], [B,Sk,Hkv,D], [B,Sk,Hkv,D]
+    void *o;                  // [B,Sq,Hq,D]
+    float *lse;               // [B,Hq,Sq] or nullptr
+    int B, Sq, Sk, Hq, Hkv;
+    float scale_log2;         // softmax scale times log2(e)
+};
+
+struct DecodeArgs {
+    const uint16_t *q;            // [B,Hq,D] bf16
+    const uint16_t *k_cache;      // [num_blocks,16,Hkv,D] bf16
+    const uint16_t *v_cache;
+    const int32_t *block_table;   // [B,max_blocks]
+    const int32_t *ctx_lens;      // [B]
+    float *part_o;                // [B,Hq,splits,D] fp32
+    float *part_lse;              // [B,Hq,splits]   fp32
+    uint16_t *o;                  // [B,Hq,D] bf16
+    float *lse;                   // [B,Hq] or nullptr
+    int B, Hq, Hkv, num_blocks, max_blocks, splits;
+    float scale_log2;
+};
+
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, bool causal, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs &a, int head_dim, bool causal, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int head_dim, hipStream_t s);
+
+}  // namespace attn

@@ -1,0 +1,278 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass over the whole path on one synthetic batch:
+  * causal GQA prefill, bf16: batch 2, 32 query / 8 KV heads, seqlen 8192,
+    head_dim 128 (attn_prefill);
+  * paged split-KV decode, bf16: batch 64, 32 / 8 heads, head_dim 128,
+    context lengths uniform in [512, 32768], 16-token blocks, shuffled table,
+    16 splits (attn_decode_paged);
+  * long-context paged decode, bf16: batch 4, 64 / 8 heads, context 131072,
+    64 splits (attn_decode_paged).
+Inputs are resident in HBM before timing; outputs and workspaces are
+preallocated.  `value` is the whole step's speed-of-light time (prefill FLOPs
+at the bf16 MFMA peak plus decode KV bytes at the HBM peak) over its measured
+time, in percent; the per-part absolute rates are in `parts`.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_HBM_BPS = 8.0e12         # MI355X HBM3E
+METRIC = "prefill attn TFLOP/s + decode KV GB/s, % of MI355X bf16/HBM peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--parts", default="prefill,decode_b64,decode_128k",
+                   help="comma-separated subset (for profiling runs)")
+    return p.parse_args()
+
+
+def decode_bytes(inp, n_q_heads):
+    """Algorithmic bytes of one paged decode call: K and V of every cached
+    token once per KV head, Q and O once, the used block-table entries and
+    the context lengths."""
+    from attention_flash_fwd_amd import inputs
+    B, Hq, D = inp.q.shape
+    kv = inputs.decode_kv_bytes(inp.ctx, inp.n_kv_heads, D)
+    used_blocks = sum((c + 15) // 16 for c in inp.ctx)
+    return kv + 2 * B * Hq * D * 2 + used_blocks * 4 + B * 4
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+PREFILL_SOURCES = ["attention_flash_fwd_amd/csrc/prefill_bf16.hip",
+                   "attention_flash_fwd_amd/csrc/gfx950.hpp"]
+
+
+def load_traffic(kernel_digest):
+    """HBM bytes per prefill launch from the committed rocprofv3 counter runs,
+    if they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "prefill_8k_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_digest") != kernel_digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(parts, pf_cfg, pf_in, dec_parts):
+    """Time the fp64 oracle on a bounded sample of each part and scale to the
+    whole step.  Returns the same %-of-peak figure as `value` (and rates)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = max(1, min(threads, 64))
+    detail = {}
+    cpu_step_s = 0.0
+    sol_s = 0.0
+    if "prefill" in parts:
+        q, k, v = pf_in
+        rng = np.random.default_rng(0)
+        B, S, Hq, D = q.shape
+        n_rows = 4096
+        rows = [(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(S))) for _ in range(n_rows)]
+        qn = q.float().cpu().numpy()
+        kn = k.float().cpu().numpy()
+        vn = v.float().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.attention_rows(qn, kn, vn, True, pf_cfg.scale, rows, nthreads=threads)
+        dt = time.perf_counter() - t0
+        flops_sample = sum(4.0 * D * (i + 1) for (_, _, i) in rows)
+        rate = flops_sample / dt
+        cpu_step_s += pf_cfg.flops() / rate
+        sol_s += pf_cfg.flops() / PEAK_BF16_FLOPS
+        detail["prefill_gflops"] = rate / 1e9
+        detail["prefill_sample"] = f"{n_rows} random query rows of all {B * Hq} heads"
+    for name, (inp, Hq, scale, nbytes) in dec_parts.items():
+        n_seq = 2
+        seqs = list(range(min(n_seq, inp.batch)))
+        qn = inp.q.float().cpu().numpy()
+        ks, vs, byts = [], [], 0
+        for b in seqs:
+            kb, vb = inp.logical_kv(b, device="cpu")
+            ks.append(kb.float().numpy())
+            vs.append(vb.float().numpy())
+            byts += 2 * kb.numel() * 2
+        t0 = time.perf_counter()
+        oracle.decode(qn[seqs], ks, vs, scale, nthreads=threads)
+        dt = time.perf_counter() - t0
+        rate = byts / dt
+        cpu_step_s += nbytes / rate
+        sol_s += nbytes / PEAK_HBM_BPS
+        detail[f"{name}_gbps"] = rate / 1e9
+        detail[f"{name}_sample"] = f"sequences {seqs}"
+    value = 100.0 * sol_s / cpu_step_s if cpu_step_s > 0 else None
+    return {"value": value, "unit": "% of MI355X peak (same step, oracle on host)",
+            "cores": threads, "kind": "oracle",
+            "sample": "; ".join(f"{k}: {v}" for k, v in detail.items() if k.endswith("sample")),
+            "step_seconds_extrapolated": cpu_step_s,
+            **{k: v for k, v in detail.items() if not k.endswith("sample")}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import attention_flash_fwd_amd as afa
+    from attention_flash_fwd_amd import _lib, inputs
+
+    _lib.load()
+    dev = torch.device("cuda:0")
+    parts = [p for p in args.parts.split(",") if p]
+
+    # ---- inputs, resident in HBM ---------------------------------------
+    pf_cfg = inputs.PREFILL_8K
+    pf_in = inputs.prefill_config_inputs(pf_cfg, device=dev) if "prefill" in parts else None
+    dec_cfgs = {"decode_b64": inputs.DECODE_B64, "decode_128k": inputs.DECODE_128K}
+    dec = {}
+    for name, cfg in dec_cfgs.items():
+        if name not in parts:
+            continue
+        inp = inputs.decode_config_inputs(cfg, device=dev)
+        ws = afa.decode_workspace(inp.q, inp.k_cache, inp.block_table, cfg.num_splits)
+        o = torch.empty_like(inp.q)
+        lse = torch.empty(inp.q.shape[:2], dtype=torch.float32, device=dev)
+        dec[name] = (cfg, inp, ws, o, lse)
+    if pf_in is not None:
+        q, k, v = pf_in
+        pf_o = torch.empty_like(q)
+        pf_lse = torch.empty((pf_cfg.batch, pf_cfg.n_q_heads, pf_cfg.seqlen), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def run_prefill():
+        afa.prefill(q, k, v, causal=True, scale=pf_cfg.scale, out=pf_o, lse_out=pf_lse)
+
+    def run_decode(name):
+        cfg, inp, ws, o, lse = dec[name]
+        afa.decode_paged(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                         num_splits=cfg.num_splits, scale=cfg.scale, out=o, lse_out=lse, workspace=ws)
+
+    runners = []
+    if pf_in is not None:
+        runners.append(("prefill", run_prefill))
+    for name in dec:
+        runners.append((name, lambda n=name: run_decode(n)))
+
+    for _ in range(args.warmup):
+        for _, fn in runners:
+            fn()
+    torch.cuda.synchronize()
+
+    # ---- timed region: events around every part of every step ----------
+    stream = torch.cuda.current_stream(dev)
+    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)] for name, _ in runners}
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        for name, fn in runners:
+            a, b = ev[name][s]
+            a.record(stream)
+            fn()
+            b.record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+
+    part_ms = {name: sum(a.elapsed_time(b) for a, b in ev[name]) / args.steps for name, _ in runners}
+    out_parts = {}
+    sol_ms = 0.0
+    if pf_in is not None:
+        fl = pf_cfg.flops()
+        tf = fl / (part_ms["prefill"] * 1e-3) / 1e12
+        sol_ms += fl / PEAK_BF16_FLOPS * 1e3
+        out_parts["prefill"] = {"workload": pf_cfg.name, "ms": part_ms["prefill"], "tflops": tf,
+                                "frac_of_peak": tf * 1e12 / PEAK_BF16_FLOPS, "flops": fl}
+    for name, (cfg, inp, ws, o, lse) in dec.items():
+        nb = decode_bytes(inp, cfg.n_q_heads)
+        gbps = nb / (part_ms[name] * 1e-3) / 1e9
+        sol_ms += nb / PEAK_HBM_BPS * 1e3
+        out_parts[name] = {"workload": cfg.name, "ms": part_ms[name], "gbps": gbps,
+                           "frac_of_peak": gbps * 1e9 / PEAK_HBM_BPS, "bytes": nb,
+                           "num_splits": cfg.num_splits, "sum_ctx": sum(inp.ctx)}
+    value = 100.0 * sol_ms / ms_per_step
+
+    roofline = None
+    if pf_in is not None:
+        digest = source_digest(PREFILL_SOURCES)
+        achieved = out_parts["prefill"]["tflops"]
+        roofline = {"bound": "mfma", "kernel": "prefill_bf16_kernel<128,true>",
+                    "achieved": achieved, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                    "frac": achieved * 1e12 / PEAK_BF16_FLOPS, "traffic": load_traffic(digest),
+                    "per_launch_flops": pf_cfg.flops(), "avg_launch_ms": part_ms["prefill"],
+                    "kernel_digest": digest}
+    decode_roofline = {
+        name: {"bound": "hbm", "achieved": p["gbps"], "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
+               "frac": p["frac_of_peak"], "per_launch_bytes": p["bytes"], "avg_launch_ms": p["ms"],
+               "note": "split + combine kernels of one attn_decode_paged call"}
+        for name, p in out_parts.items() if name != "prefill"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        dec_parts = {name: (inp, cfg.n_q_heads, cfg.scale, out_parts[name]["bytes"])
+                     for name, (cfg, inp, ws, o, lse) in dec.items()}
+        cpu = cpu_baseline(parts, pf_cfg, pf_in, dec_parts)
+
+    workload = " + ".join(out_parts[p]["workload"] for p in out_parts)
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "% of peak (step speed-of-light time / measured step time)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid N(0,1), bf16; shuffled paged KV cache)",
+        "config": {"workload": workload, "parts": list(out_parts)},
+        "parts": out_parts,
+        "roofline": roofline,
+        "roofline_decode": decode_roofline,
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": wall,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

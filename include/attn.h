@@ -1,0 +1,189 @@
+/*
+ * attn.h -- exact attention forward on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libattn.so.  Two operations:
+ *
+ *   attn_prefill       exact scaled-dot-product attention over whole
+ *                      sequences (optionally causal, grouped-query heads),
+ *                      computed the FlashAttention way: Q/K/V tiles are
+ *                      staged on chip, QK^T and PV run on the matrix cores,
+ *                      a running row max and row sum rescale the partial
+ *                      output tile by tile, and the N x N score matrix never
+ *                      reaches device memory.
+ *                      ("推理加速" interview notes, section FlashAttention:
+ *                      tiling, on-chip block attention, online softmax, only
+ *                      the final output written back, mathematically equal to
+ *                      standard attention; chenyy20.com "抱infra脚", section
+ *                      Flash Attention 基本原理 / 核心技术: tiling, online
+ *                      softmax and kernel fusion of QK + softmax + PV.)
+ *
+ *   attn_decode_paged  one new query token per sequence against a paged KV
+ *                      cache, Flash-Decoding style: the cached keys of each
+ *                      sequence are cut into chunks processed in parallel,
+ *                      each producing a partial output and its log-sum-exp,
+ *                      and a second small kernel merges the partials with the
+ *                      online-softmax formula, accumulating in fp32.
+ *                      ("GPU Kernel 调度：大模型推理的拐点 2026", paragraphs on
+ *                      Flash Decoding and its reduce-kernel cost; chenyy20.com
+ *                      "抱infra脚", section Paged Attention: fixed-size cache
+ *                      blocks mapped through a block table.)
+ *
+ * Conventions shared by both operations
+ * -------------------------------------
+ *  - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *    allocates nothing, keeps no state between calls and may be called from
+ *    several host threads at once.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without waiting.  Outputs are valid once the stream has
+ *    reached that point.
+ *  - Tensors are contiguous, row-major, head_dim innermost.  bf16 is the
+ *    IEEE-style bfloat16 (1-8-7) bit pattern in a uint16.
+ *  - Query head h uses key/value head h / (n_q_heads / n_kv_heads)
+ *    (consecutive query heads share a KV head).
+ *  - Causal visibility is bottom-right aligned: key j is visible to query i
+ *    iff j <= i + (seqlen_k - seqlen_q).  A query row with no visible key
+ *    gets O = 0 and lse = -inf.
+ *  - lse is the natural-log log-sum-exp of the visible scaled scores
+ *    (scale * q.k), in fp32.
+ *  - Internally: scores, softmax statistics and output accumulators are
+ *    fp32; for bf16 inputs the probabilities are rounded to bf16 (nearest
+ *    even) as the PV matrix-core operand and O is rounded to bf16 (nearest
+ *    even) once at the end.  The fp32 path never rounds below fp32.
+ *  - Errors are returned as attn_status_t; nothing is thrown across the ABI.
+ *    All argument checks run on the host before any HIP call: on a non-OK
+ *    status nothing has been enqueued and no output has been touched, except
+ *    ATTN_ERR_LAUNCH (the launch itself failed; outputs are undefined).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    ATTN_ERR_ALIGN = 2,       /* a tensor pointer is not 16-byte aligned          */
+    ATTN_ERR_SHAPE = 3,       /* negative size, heads not a multiple, bad sizes   */
+    ATTN_ERR_DTYPE = 4,       /* unknown dtype code                               */
+    ATTN_ERR_UNSUPPORTED = 5, /* valid but not implemented (head_dim, block_size,
+                                 dtype for this operation, num_splits range)      */
+    ATTN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required       */
+    ATTN_ERR_LAUNCH = 7       /* the HIP launch reported an error                 */
+} attn_status_t;
+
+typedef enum {
+    ATTN_BF16 = 0,            /* bf16 inputs and output                           */
+    ATTN_F32 = 1              /* fp32 inputs and output                           */
+} attn_dtype_t;
+
+typedef void *attn_stream_t;  /* a hipStream_t */
+
+/* Largest num_splits accepted by attn_decode_paged. */
+#define ATTN_MAX_SPLITS 256
+
+/*
+ * attn_prefill -- O = softmax(scale * Q K^T [+ causal mask]) V per (batch, head).
+ *
+ *   q    [batch, seqlen_q, n_q_heads,  head_dim]   dtype
+ *   k    [batch, seqlen_k, n_kv_heads, head_dim]   dtype
+ *   v    [batch, seqlen_k, n_kv_heads, head_dim]   dtype
+ *   o    [batch, seqlen_q, n_q_heads,  head_dim]   dtype, written
+ *   lse  [batch, n_q_heads, seqlen_q]              fp32, written; may be NULL
+ *
+ * Supported: dtype ATTN_BF16 or ATTN_F32; head_dim 64 or 128.
+ * batch == 0 or seqlen_q == 0 is a no-op (pointers may then be NULL);
+ * seqlen_k == 0 gives O = 0, lse = -inf.  q, k, v, o must be 16-byte
+ * aligned, lse 4-byte aligned.  q/k/v must not overlap o/lse.
+ * Returns ATTN_ERR_SHAPE for negative sizes, non-positive head counts,
+ * n_q_heads % n_kv_heads != 0, or element counts above 2^31 per tensor;
+ * ATTN_ERR_UNSUPPORTED for another head_dim; ATTN_ERR_DTYPE for an unknown
+ * dtype code.
+ */
+attn_status_t attn_prefill(const void *q, const void *k, const void *v,
+                           void *o, float *lse,
+                           int batch, int seqlen_q, int seqlen_k,
+                           int n_q_heads, int n_kv_heads, int head_dim,
+                           int causal, float scale, attn_dtype_t dtype,
+                           attn_stream_t stream);
+
+/*
+ * attn_decode_num_splits -- the number of key chunks per sequence that
+ * attn_decode_paged will use for these arguments.  num_splits >= 1 is
+ * returned unchanged (after the range check of attn_decode_paged);
+ * num_splits <= 0 asks for the library's choice, which depends only on the
+ * arguments given here (never on device data): enough chunks to occupy the
+ * GPU, none shorter than 256 tokens.  Returns 0 for invalid arguments.
+ */
+int attn_decode_num_splits(int batch, int n_kv_heads, int max_blocks_per_seq,
+                           int block_size, int num_splits);
+
+/*
+ * attn_decode_workspace_bytes -- size of the scratch buffer attn_decode_paged
+ * needs for these arguments: the per-chunk partial outputs
+ * [batch, n_q_heads, splits, head_dim] fp32 followed by their log-sum-exps
+ * [batch, n_q_heads, splits] fp32 (splits = attn_decode_num_splits(...)).
+ * Returns 0 for invalid arguments.
+ */
+size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                   int max_blocks_per_seq, int block_size, int num_splits);
+
+/*
+ * attn_decode_paged -- one query token per sequence over a paged KV cache.
+ *
+ *   q            [batch, n_q_heads, head_dim]                       bf16
+ *   k_cache      [num_blocks, block_size, n_kv_heads, head_dim]     bf16
+ *   v_cache      [num_blocks, block_size, n_kv_heads, head_dim]     bf16
+ *   block_table  [batch, max_blocks_per_seq] int32: physical block of each
+ *                logical block; entries past a sequence's last block are
+ *                ignored (conventionally -1)
+ *   ctx_lens     [batch] int32: cached tokens of each sequence; token t of
+ *                sequence b sits at slot t % block_size of physical block
+ *                block_table[b][t / block_size]
+ *   o            [batch, n_q_heads, head_dim] bf16, written
+ *   lse          [batch, n_q_heads] fp32, written; may be NULL
+ *   workspace    device scratch of at least attn_decode_workspace_bytes(...)
+ *                bytes, 256-byte aligned; its contents on entry do not matter
+ *
+ * Every cached key of a sequence is visible to its query.  Sequence b's keys
+ * are cut into `splits` chunks of equal length (a multiple of block_size,
+ * the last one shorter or empty); each chunk is one partial, merged with the
+ * log-sum-exp formula.  The result does not depend on the number of splits
+ * beyond fp32 rounding.  Cache slots past ctx_lens[b] are never read, so
+ * they may hold anything, NaN included.
+ *
+ * Supported: head_dim 64 or 128; block_size 16; n_q_heads / n_kv_heads <= 16;
+ * num_splits in [1, ATTN_MAX_SPLITS] or <= 0 for the library's choice.
+ * ctx_lens[b] == 0 gives O = 0, lse = -inf.
+ * Device-side contract violations do not fault: a sequence whose ctx_lens
+ * entry is negative or exceeds max_blocks_per_seq * block_size, or whose
+ * needed block ids fall outside [0, num_blocks), gets NaN in o and lse.
+ * Returns ATTN_ERR_WORKSPACE if workspace is NULL or workspace_bytes is too
+ * small, and the other codes as for attn_prefill.
+ */
+attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *block_table, const int32_t *ctx_lens,
+                                void *o, float *lse,
+                                int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                int num_blocks, int block_size, int max_blocks_per_seq,
+                                int num_splits, float scale,
+                                void *workspace, size_t workspace_bytes,
+                                attn_stream_t stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *attn_status_string(attn_status_t status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int attn_abi_version(void);
+
+#define ATTN_ABI_VERSION ((1 << 16) | 0)
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,156 @@
+"""The C-ABI library on the host (no GPU, no compute calls).
+
+Checks that libattn.so loads, exports every function include/attn.h declares,
+and rejects bad arguments with the documented status codes.  Rejected calls
+return before any HIP call, so the device pointers here are fake values that
+are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+from attention_flash_fwd_amd import _lib  # noqa: E402
+
+OK, NULL, ALIGN, SHAPE, DTYPE, UNSUP, WORKSPACE = 0, 1, 2, 3, 4, 5, 6
+FAKE = 0x10000          # 64 KiB: 16-byte aligned, never dereferenced
+FAKE_MIS = 0x10008      # 8-byte aligned only
+BF16, F32 = 0, 1
+
+
+def header_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libattn.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    for name in ("attn_prefill", "attn_decode_paged", "attn_decode_workspace_bytes",
+                 "attn_decode_num_splits", "attn_status_string", "attn_abi_version"):
+        assert name in fns
+    assert set(fns) == set(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_exports_are_c_symbols():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in header_functions():
+        assert name in syms, f"{name} not exported with C linkage"
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.attn_abi_version() == (1 << 16)
+    for code in range(8):
+        s = lib.attn_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.attn_status_string(99).decode() == "unknown status"
+
+
+def prefill(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Sq=8, Sk=8, Hq=4, Hkv=2, D=128,
+            causal=1, scale=0.1, dtype=BF16):
+    P = ctypes.c_void_p
+    return lib.attn_prefill(P(q), P(k), P(v), P(o), P(lse), B, Sq, Sk, Hq, Hkv, D, causal,
+                            scale, dtype, P(0))
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, dtype=7) == DTYPE
+    assert prefill(lib, D=96) == UNSUP
+    assert prefill(lib, D=256) == UNSUP
+    assert prefill(lib, Hq=6, Hkv=4) == SHAPE
+    assert prefill(lib, Hkv=0) == SHAPE
+    assert prefill(lib, B=-1) == SHAPE
+    assert prefill(lib, Sq=-3) == SHAPE
+    assert prefill(lib, Sk=-1) == SHAPE
+    assert prefill(lib, B=1 << 10, Sq=1 << 14, Hq=1 << 4) == SHAPE    # 2^31 elements
+    assert prefill(lib, q=0) == NULL
+    assert prefill(lib, o=0) == NULL
+    assert prefill(lib, k=0) == NULL
+    assert prefill(lib, v=0) == NULL
+    assert prefill(lib, q=FAKE_MIS) == ALIGN
+    assert prefill(lib, o=FAKE_MIS) == ALIGN
+    assert prefill(lib, v=FAKE_MIS) == ALIGN
+    assert prefill(lib, lse=FAKE + 2) == ALIGN
+    # Empty problems are no-ops that need no pointers at all.
+    assert prefill(lib, q=0, k=0, v=0, o=0, lse=0, B=0) == OK
+    assert prefill(lib, q=0, k=0, v=0, o=0, lse=0, Sq=0) == OK
+
+
+def decode(lib, q=FAKE, kc=FAKE, vc=FAKE, tbl=FAKE, ctx=FAKE, o=FAKE, lse=FAKE, B=2, Hq=8, Hkv=2,
+           D=128, nblocks=10, bs=16, max_blocks=5, splits=4, scale=0.1, ws=FAKE, ws_bytes=None):
+    P = ctypes.c_void_p
+    if ws_bytes is None:
+        ws_bytes = lib.attn_decode_workspace_bytes(B, Hq, Hkv, D, max_blocks, bs, splits)
+    return lib.attn_decode_paged(P(q), P(kc), P(vc), P(tbl), P(ctx), P(o), P(lse), B, Hq, Hkv, D,
+                                 nblocks, bs, max_blocks, splits, scale, P(ws), ws_bytes, P(0))
+
+
+def test_decode_validation(lib):
+    assert decode(lib, D=80) == UNSUP
+    assert decode(lib, bs=32) == UNSUP
+    assert decode(lib, Hq=34, Hkv=2) == UNSUP        # 17 query heads per KV head
+    assert decode(lib, splits=257) == UNSUP
+    assert decode(lib, Hq=6, Hkv=4) == SHAPE
+    assert decode(lib, B=-1) == SHAPE
+    assert decode(lib, nblocks=-1) == SHAPE
+    assert decode(lib, q=0) == NULL
+    assert decode(lib, tbl=0) == NULL
+    assert decode(lib, ctx=0) == NULL
+    assert decode(lib, kc=0) == NULL
+    assert decode(lib, o=0) == NULL
+    assert decode(lib, q=FAKE_MIS) == ALIGN
+    assert decode(lib, kc=FAKE_MIS) == ALIGN
+    assert decode(lib, tbl=FAKE + 2) == ALIGN
+    assert decode(lib, ws=0) == WORKSPACE
+    need = lib.attn_decode_workspace_bytes(2, 8, 2, 128, 5, 16, 4)
+    assert decode(lib, ws_bytes=need - 1) == WORKSPACE
+    assert decode(lib, B=0, q=0, o=0, tbl=0, ctx=0) == OK
+
+
+def test_workspace_and_split_rules(lib):
+    # Explicit split counts pass through; the workspace holds fp32 partial
+    # outputs and log-sum-exps for every (sequence, query head, split).
+    for B, Hq, Hkv, D, mb, S in [(64, 32, 8, 128, 2048, 16), (4, 64, 8, 128, 8192, 64),
+                                 (1, 1, 1, 64, 1, 1)]:
+        assert lib.attn_decode_num_splits(B, Hkv, mb, 16, S) == S
+        nbytes = lib.attn_decode_workspace_bytes(B, Hq, Hkv, D, mb, 16, S)
+        assert nbytes >= B * Hq * S * (D + 1) * 4
+        assert nbytes < B * Hq * S * (D + 1) * 4 + 1024
+    # Automatic choice: in [1, 256], never chunks shorter than 256 tokens,
+    # and enough workgroups to cover the GPU when the context allows it.
+    for B, Hkv, mb in [(1, 1, 1), (4, 8, 8192), (64, 8, 2048), (1, 8, 64), (256, 8, 4)]:
+        s = lib.attn_decode_num_splits(B, Hkv, mb, 16, 0)
+        assert 1 <= s <= 256
+        assert s <= max(1, (mb * 16 + 255) // 256)
+        if (mb * 16) // 256 >= 256:
+            assert B * Hkv * s >= 1024
+    assert lib.attn_decode_num_splits(-1, 8, 4, 16, 0) == 0
+    assert lib.attn_decode_workspace_bytes(1, 0, 1, 128, 4, 16, 1) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    import attention_flash_fwd_amd as afa
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        afa.prefill(q, q[:, :, :1].contiguous(), q[:, :, :1].contiguous())

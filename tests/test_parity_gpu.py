@@ -1,0 +1,321 @@
+"""Parity of the HIP path with the fp64 oracle, on the GPU.
+
+Every case draws seeded inputs from attention_flash_fwd_amd.inputs, runs the
+library through its C ABI (the Python binding only marshals pointers), and
+compares with the oracle on the same bytes:
+  bf16 output  max-abs <= 2e-2, mean-abs <= 2e-3; lse max-abs <= 1e-4
+  fp32 path    max-abs <= 1e-5 (output and lse)
+Small shapes are compared in full; the full-size workloads are compared on
+sampled rows (prefill) or sampled sequences (decode) that the oracle computes
+one by one, plus properties that hold at any size.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.helpers import (BF16_LSE_ABS, BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, check_lse,
+                           check_o, to_np)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def afa(cuda):
+    import attention_flash_fwd_amd as afa_mod
+    from attention_flash_fwd_amd import _lib
+    _lib.load()
+    return afa_mod
+
+
+def gen_prefill(B, Sq, Sk, Hq, Hkv, D, dtype, seed):
+    from attention_flash_fwd_amd import inputs
+    return inputs.prefill_inputs(B, Sq, Sk, Hq, Hkv, D, dtype, seed, device="cpu")
+
+
+def run_prefill(afa, q, k, v, causal, scale):
+    o, lse = afa.prefill(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return to_np(o), to_np(lse)
+
+
+# ------------------------------------------------------------- prefill ---
+def test_tiny_noncausal_f32_config(afa):
+    from attention_flash_fwd_amd import inputs
+    cfg = inputs.TINY_F32
+    say(f"case {cfg.name}")
+    q, k, v = inputs.prefill_config_inputs(cfg)
+    o, lse = run_prefill(afa, q, k, v, cfg.causal, cfg.scale)
+    o_ref, lse_ref = oracle.attention(q.numpy(), k.numpy(), v.numpy(), cfg.causal, cfg.scale)
+    check_o(o, o_ref, F32_MAX_ABS)
+    check_lse(lse, lse_ref, F32_MAX_ABS)
+
+
+@pytest.mark.parametrize("B,Sq,Sk,Hq,Hkv,D,causal", [
+    (1, 200, 200, 4, 2, 128, True),
+    (2, 129, 129, 2, 1, 64, True),
+    (1, 100, 300, 2, 2, 128, True),
+    (1, 77, 33, 2, 1, 64, False),
+])
+def test_prefill_f32(afa, B, Sq, Sk, Hq, Hkv, D, causal):
+    say(f"case f32 B{B} Sq{Sq} Sk{Sk} Hq{Hq} Hkv{Hkv} D{D} causal{causal}")
+    q, k, v = gen_prefill(B, Sq, Sk, Hq, Hkv, D, torch.float32, 7)
+    scale = 1 / math.sqrt(D)
+    o, lse = run_prefill(afa, q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.attention(q.numpy(), k.numpy(), v.numpy(), causal, scale)
+    check_o(o, o_ref, F32_MAX_ABS)
+    check_lse(lse, lse_ref, F32_MAX_ABS)
+
+
+PREFILL_BF16_CASES = [
+    (1, 1, 1, 1, 1, 128, True),
+    (1, 17, 17, 2, 1, 128, True),
+    (1, 127, 127, 4, 4, 64, False),
+    (1, 129, 129, 8, 2, 128, True),
+    (2, 200, 200, 4, 2, 128, True),
+    (1, 257, 257, 8, 8, 64, True),
+    (1, 1000, 1000, 4, 1, 128, True),
+    (2, 100, 300, 4, 2, 128, True),     # Sq < Sk: bottom-right causal alignment
+    (1, 300, 100, 2, 1, 128, True),     # Sq > Sk: leading rows see no key
+    (3, 333, 333, 6, 3, 64, False),
+    (2, 300, 300, 16, 4, 128, True),    # (batch, KV head) pairs a multiple of 8
+    (1, 384, 384, 32, 8, 128, True),
+    (1, 130, 70, 4, 2, 128, False),
+]
+
+
+@pytest.mark.parametrize("B,Sq,Sk,Hq,Hkv,D,causal", PREFILL_BF16_CASES)
+def test_prefill_bf16(afa, B, Sq, Sk, Hq, Hkv, D, causal):
+    say(f"case bf16 B{B} Sq{Sq} Sk{Sk} Hq{Hq} Hkv{Hkv} D{D} causal{causal}")
+    q, k, v = gen_prefill(B, Sq, Sk, Hq, Hkv, D, torch.bfloat16, 11 + Sq)
+    scale = 1 / math.sqrt(D)
+    o, lse = run_prefill(afa, q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.attention(to_np(q), to_np(k), to_np(v), causal, scale)
+    check_o(o, o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(lse, lse_ref, BF16_LSE_ABS)
+
+
+def test_prefill_empty_keys(afa):
+    say("case bf16 Sk=0")
+    q = torch.randn(1, 64, 2, 128).to(torch.bfloat16).cuda()
+    k = torch.zeros(1, 0, 1, 128, dtype=torch.bfloat16, device="cuda")
+    o, lse = afa.prefill(q, k, k.clone(), causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_prefill_empty_batch(afa):
+    q = torch.zeros(0, 8, 2, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(0, 8, 1, 128, dtype=torch.bfloat16, device="cuda")
+    o, lse = afa.prefill(q, k, k.clone())
+    assert o.shape == q.shape and lse.shape == (0, 2, 8)
+
+
+def sample_rows(B, S, Hq, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in range(B):
+        for h in (0, Hq - 1):
+            for i in (0, 1, 127, 128, 129, S // 2, S - 2, S - 1):
+                rows.add((b, h, i))
+    while len(rows) < n:
+        rows.add((int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(S))))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("cfg_name", ["causal_gqa_prefill_b4_h32kv8_s2048_d128_bf16",
+                                      "causal_gqa_prefill_b2_h32kv8_s8192_d128_bf16"])
+def test_prefill_full_size_sampled(afa, cfg_name):
+    from attention_flash_fwd_amd import inputs
+    cfg = inputs.CONFIGS[cfg_name]
+    say(f"case {cfg.name} (sampled rows)")
+    q, k, v = inputs.prefill_config_inputs(cfg, device="cuda")
+    o, lse = afa.prefill(q, k, v, causal=cfg.causal, scale=cfg.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    # Causal row 0 of every head is exactly V[0] of its KV head.
+    G = cfg.n_q_heads // cfg.n_kv_heads
+    v0 = v[:, 0].repeat_interleave(G, dim=1)
+    assert torch.equal(o[:, 0], v0)
+    rows = sample_rows(cfg.batch, cfg.seqlen, cfg.n_q_heads, 400, 123)
+    o_ref, lse_ref = oracle.attention_rows(to_np(q), to_np(k), to_np(v), cfg.causal, cfg.scale, rows)
+    on, ln = to_np(o), to_np(lse)
+    got_o = np.stack([on[b, i, h] for (b, h, i) in rows])
+    got_l = np.array([ln[b, h, i] for (b, h, i) in rows])
+    check_o(got_o, o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(got_l, lse_ref, BF16_LSE_ABS)
+
+
+def test_prefill_invariants(afa):
+    say("case prefill invariants")
+    B, S, Hq, Hkv, D = 2, 300, 8, 2, 128
+    q, k, v = gen_prefill(B, S, S, Hq, Hkv, D, torch.bfloat16, 99)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    o1, l1 = afa.prefill(qc, kc, vc, causal=True)
+    o2, l2 = afa.prefill(qc, kc, vc, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "repeat run differs"
+    # GQA == MHA with each KV head repeated for its query heads (same arithmetic).
+    G = Hq // Hkv
+    o3, l3 = afa.prefill(qc, kc.repeat_interleave(G, 2).contiguous(),
+                         vc.repeat_interleave(G, 2).contiguous(), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3) and torch.equal(l1, l3), "GQA differs from repeated-KV MHA"
+    # Causal row 0 is V[0] exactly.
+    assert torch.equal(o1[:, 0], vc[:, 0].repeat_interleave(G, 1))
+    # Constant V per KV head -> every output row equals that constant (to bf16 rounding of P).
+    cst = torch.randn(B, 1, Hkv, D).to(torch.bfloat16).cuda()
+    o4, _ = afa.prefill(qc, kc, cst.expand(B, S, Hkv, D).contiguous(), causal=True)
+    torch.cuda.synchronize()
+    want = cst.expand(B, S, Hkv, D).repeat_interleave(G, 2).float()
+    assert (o4.float() - want).abs().max().item() <= 2e-2
+    # scale = 0: mean of the visible values (closed form), lse = ln(#visible).
+    o5, l5 = afa.prefill(qc, kc, vc, causal=True, scale=0.0)
+    torch.cuda.synchronize()
+    cnt = torch.arange(1, S + 1, device="cuda", dtype=torch.float32)
+    mean = vc.float().cumsum(1) / cnt[None, :, None, None]
+    assert (o5.float() - mean.repeat_interleave(G, 2)).abs().max().item() <= 2e-2
+    assert (l5 - cnt.log()[None, None, :]).abs().max().item() <= 1e-5
+
+
+# -------------------------------------------------------------- decode ---
+def gen_decode(ctx, Hq, Hkv, D, seed, device="cuda", spare_blocks=3, table_pad=2):
+    from attention_flash_fwd_amd import inputs
+    return inputs.decode_inputs(ctx, Hq, Hkv, D, seed=seed, device=device,
+                                spare_blocks=spare_blocks, table_pad=table_pad)
+
+
+def decode_oracle(inp, scale, seqs=None):
+    seqs = range(inp.batch) if seqs is None else seqs
+    q = to_np(inp.q)
+    o_all, l_all = [], []
+    for b in seqs:
+        kb, vb = inp.logical_kv(b, device="cpu")
+        o, l = oracle.decode(q[b:b + 1], [to_np(kb)], [to_np(vb)], scale)
+        o_all.append(o[0])
+        l_all.append(l[0])
+    return np.stack(o_all), np.stack(l_all)
+
+
+def run_decode(afa, inp, splits, scale=None):
+    o, lse = afa.decode_paged(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                              num_splits=splits, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("ctx,Hq,Hkv,D,splits", [
+    ([1, 15, 16, 17, 513], 8, 2, 128, 1),
+    ([1, 15, 16, 17, 513], 8, 2, 128, 2),
+    ([1, 15, 16, 17, 513], 8, 2, 128, 7),
+    ([1, 15, 16, 17, 513], 8, 2, 128, 64),
+    ([33, 700, 1024, 5], 8, 8, 128, 3),      # G = 1
+    ([100, 2000], 32, 8, 128, 16),           # G = 4
+    ([257, 1500, 31], 64, 8, 128, 8),        # G = 8
+    ([900, 64, 1], 16, 1, 128, 5),           # G = 16
+    ([300, 45], 8, 2, 64, 4),                # D = 64
+    ([4096, 333], 8, 1, 64, 0),              # automatic split count
+])
+def test_decode_small(afa, ctx, Hq, Hkv, D, splits):
+    say(f"case decode ctx{ctx} Hq{Hq} Hkv{Hkv} D{D} splits{splits}")
+    inp = gen_decode(ctx, Hq, Hkv, D, seed=len(ctx) * 10 + Hq)
+    scale = 1 / math.sqrt(D)
+    o, lse = run_decode(afa, inp, splits)
+    o_ref, l_ref = decode_oracle(inp, scale)
+    check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse), l_ref, BF16_LSE_ABS)
+
+
+def test_decode_zero_context(afa):
+    say("case decode ctx 0")
+    inp = gen_decode([0, 20, 0], 8, 2, 128, seed=3)
+    o, lse = run_decode(afa, inp, 4)
+    assert torch.all(o[0] == 0) and torch.all(o[2] == 0)
+    assert torch.all(torch.isneginf(lse[0])) and torch.all(torch.isneginf(lse[2]))
+    o_ref, l_ref = decode_oracle(inp, 1 / math.sqrt(128), seqs=[1])
+    check_o(to_np(o[1:2]), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+
+
+def test_decode_split_invariance_and_permutation(afa):
+    say("case decode split invariance / block permutation")
+    inp = gen_decode([1000, 37, 4097], 32, 8, 128, seed=5)
+    outs = [run_decode(afa, inp, s) for s in (1, 3, 16, 64)]
+    for o, l in outs[1:]:
+        assert (o.float() - outs[0][0].float()).abs().max().item() <= 1e-2
+        assert (l - outs[0][1]).abs().max().item() <= 1e-5
+    # Same logical cache under another physical placement -> bit-identical output.
+    nb = inp.k_cache.shape[0]
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(1)).cuda()
+    k2 = torch.empty_like(inp.k_cache)
+    v2 = torch.empty_like(inp.v_cache)
+    k2[perm] = inp.k_cache
+    v2[perm] = inp.v_cache
+    tbl = inp.block_table.long()
+    tbl2 = torch.where(tbl >= 0, perm[tbl.clamp(min=0)], tbl).to(torch.int32).contiguous()
+    o_a, l_a = run_decode(afa, inp, 16)
+    o_b, l_b = afa.decode_paged(inp.q, k2, v2, tbl2, inp.ctx_lens, num_splits=16)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b)
+    o_c, l_c = run_decode(afa, inp, 16)
+    assert torch.equal(o_a, o_c) and torch.equal(l_a, l_c), "repeat run differs"
+
+
+def test_decode_contract_violations_give_nan(afa):
+    say("case decode bad block ids / oversize ctx")
+    inp = gen_decode([40, 40, 40], 8, 2, 128, seed=8, table_pad=0)
+    tbl = inp.block_table.clone()
+    tbl[0, 1] = inp.k_cache.shape[0] + 5          # block id past the pool
+    tbl[1, 2] = -7                                 # negative block id
+    ctx = inp.ctx_lens.clone()
+    o, lse = afa.decode_paged(inp.q, inp.k_cache, inp.v_cache, tbl, ctx, num_splits=2)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[0]).all() and torch.isnan(lse[0]).all()
+    assert torch.isnan(o[1]).all() and torch.isnan(lse[1]).all()
+    assert torch.isfinite(o[2]).all() and torch.isfinite(lse[2]).all()
+    ctx2 = inp.ctx_lens.clone()
+    ctx2[2] = inp.block_table.shape[1] * 16 + 1  # more tokens than the table can hold
+    o, lse = afa.decode_paged(inp.q, inp.k_cache, inp.v_cache, inp.block_table, ctx2, num_splits=2)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[2]).all() and torch.isfinite(o[0]).all()
+
+
+def test_decode_matches_last_row_of_causal_prefill(afa):
+    say("case decode == last causal prefill row")
+    L, Hq, Hkv, D = 777, 32, 8, 128
+    inp = gen_decode([L], Hq, Hkv, D, seed=12)
+    kb, vb = inp.logical_kv(0)
+    qp = torch.randn(1, L, Hq, D, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16).cuda()
+    qp[0, L - 1] = inp.q[0]
+    op, lp = afa.prefill(qp, kb[None].contiguous(), vb[None].contiguous(), causal=True)
+    od, ld = run_decode(afa, inp, 5)
+    assert (op[0, L - 1].float() - od[0].float()).abs().max().item() <= 2e-2
+    assert (lp[0, :, L - 1] - ld[0]).abs().max().item() <= 1e-4
+
+
+@pytest.mark.parametrize("cfg_name,nseq", [("paged_decode_b64_h32kv8_d128_ctx512-32768_bf16", 8),
+                                           ("paged_decode_b4_h64kv8_d128_ctx131072_bf16", 2)])
+def test_decode_full_size_sampled(afa, cfg_name, nseq):
+    from attention_flash_fwd_amd import inputs
+    cfg = inputs.CONFIGS[cfg_name]
+    say(f"case {cfg.name} (sampled sequences, num_splits={cfg.num_splits})")
+    inp = inputs.decode_config_inputs(cfg, device="cuda")
+    o, lse = run_decode(afa, inp, cfg.num_splits)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(77)
+    ctx = np.array(inp.ctx)
+    seqs = sorted(set([int(np.argmax(ctx)), int(np.argmin(ctx))] +
+                      [int(x) for x in rng.choice(len(ctx), size=nseq, replace=False)]))[:max(nseq, 2)]
+    o_ref, l_ref = decode_oracle(inp, cfg.scale, seqs)
+    check_o(to_np(o)[seqs], o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse)[seqs], l_ref, BF16_LSE_ABS)
+    del inp
+    torch.cuda.empty_cache()
