@@ -88,4 +88,45 @@ __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return b
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+// Values the compiler cannot prove wave-uniform but that are: move them to
+// scalar registers so that buffer descriptors and LDS bases stay scalar.
+// (readfirstlane returns a signed int: go through uint32_t so that nothing
+// is sign-extended into the upper address bits.)
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+__device__ __forceinline__ void *uniform_ptr(const void *p)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = uniform_u32((uint32_t)a);
+    const uint64_t hi = uniform_u32((uint32_t)(a >> 32));
+    return reinterpret_cast<void *>(lo | (hi << 32));
+}
+
+// Raw buffer descriptor over [base, base + bytes): loads at offsets past the
+// end return zero (word 3 = 0x00020000, the gfx9 raw-buffer format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(base), (short)0, (int)uniform_u32(bytes), 0x00020000);
+}
+
+// 16 bytes per lane from buffer offset voff straight into LDS: the wave's 64
+// lanes fill the 1 KiB at lds (lane i at lds + 16 i).  Completion is tracked
+// by vmcnt like any vector-memory load.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane i receives element i % 4 of the 8-byte words read by lanes
+// i / 4 + 4 e (e = 0..3) of its group.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t *p)
+{
+    typedef short i16x4_t __attribute__((ext_vector_type(4)));
+    i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t *)(p));
+    return __builtin_bit_cast(u32x2_t, r);
+}
+
 }  // namespace attn

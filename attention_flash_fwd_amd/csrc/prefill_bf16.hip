@@ -10,28 +10,37 @@
 // K/V blocks pipelined, row-max / row-sum reductions):
 //
 //   one workgroup = 128 query rows of one (batch, query head), 4 waves of 32
-//   rows each.  K/V tiles of 64 keys stream through a two-stage LDS ring;
-//   while the matrix cores work on tile j the next tile's global loads are in
-//   flight.  Per tile and wave:
-//     S^T = K Q^T         (32x32x16 bf16 MFMA; one lane = one query row, so
-//                          the row max / row sum are in-lane reductions plus
-//                          one exchange between the two wave halves)
-//     causal / ragged mask (only on tiles that cross the diagonal or the end)
-//     online softmax in the exp2 domain (scale*log2e folded into one multiply)
-//                          with lazy rescaling: the running max used as the
-//                          exponent reference only moves when the true max
-//                          has grown by more than 2^8, so most tiles skip the
-//                          O rescale; results are identical up to rounding
-//     P -> bf16 (RNE), kept in registers: the S^T accumulator layout is
-//                          exactly the B-operand layout of O^T = V^T P^T once
-//                          the keys are permuted consistently in V^T
-//     O^T += V^T P^T      (32x32x16 bf16 MFMA, V stored transposed in LDS)
+//   rows each.  K/V tiles of 64 keys stream through a two-stage LDS ring fed
+//   by buffer loads that write LDS directly (no register staging; rows past
+//   the end of the sequence read as zero), so tile j+1 is in flight while
+//   tile j is computed.  Per tile and wave:
+//     S^T = K Q^T          32x32x16 bf16 MFMA; one lane = one query row, so
+//                          the row max is an in-lane reduction plus one
+//                          exchange between the two wave halves
+//     causal / ragged mask only on tiles that cross the diagonal or the end
+//     online softmax       exp2 domain: p = 2^(s * scale*log2e - m) is one
+//                          FMA + one v_exp_f32 per score.  Lazy rescaling:
+//                          the exponent reference m only moves when the row
+//                          max has grown by more than 2^8, so most tiles skip
+//                          rescaling O; the result is the same up to rounding
+//     P -> bf16 (RNE)      kept in registers; the S^T accumulator layout is
+//                          the B operand of O^T = V^T P^T once the keys of
+//                          each MFMA are taken in the accumulator's order.
+//                          The row sum l accumulates the fp32 P, so lse keeps
+//                          fp32 accuracy
+//     O^T += V^T P^T       32x32x16 bf16 MFMA; V stays row-major in LDS and
+//                          its transposed operand comes from ds_read_b64_tr_b16
 //   Epilogue: O = O / l rounded to bf16, lse = (m + log2 l) * ln 2.
+//
+// LDS tiles are row-major with 16-byte chunks XOR-swizzled per row so that
+// both the K row reads and the transposing V reads spread over all banks.
 //
 // Grid: one workgroup per (q-tile, query head, batch).  Workgroup ids are
 // mapped so that the longest causal q-tiles start first and all query heads
 // of one (batch, KV head) land on the same XCD (ids go round-robin over the
 // 8 XCDs), where its K/V stays in that XCD's L2.
+#include <type_traits>
+
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
@@ -41,26 +50,22 @@ namespace {
 constexpr int kBR = 128;      // query rows per workgroup
 constexpr int kBC = 64;       // keys per K/V tile
 constexpr int kThreads = 256;
+constexpr int kWaves = 4;
 
 template <int D>
-struct Smem {
-    static constexpr int kPitch = D + 8;            // K row pitch (bf16), breaks bank aliasing
-    static constexpr int vPitch = kBC + 8;          // V^T row pitch (bf16)
-    static constexpr int kElems = kBC * kPitch;
-    static constexpr int vElems = D * vPitch;
-    static constexpr int stage = kElems + vElems;   // one K tile + one V^T tile
-    static constexpr int kChunks = kBC * D / 8 / kThreads;  // 16-byte K chunks per thread
+struct Tile {
+    static constexpr int cpr = D / 8;                     // 16-byte chunks per row
+    static constexpr int elems = kBC * D;                 // bf16 elements per K or V tile
+    static constexpr int loads_per_wave = kBC * cpr / 64 / kWaves;   // 1 KiB LDS-direct loads
+    // Physical chunk of logical chunk c in row r.
+    static __device__ __forceinline__ int swz(int r, int c)
+    {
+        if constexpr (D == 128)
+            return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+        else
+            return c ^ ((r >> 1) & 7);
+    }
 };
-
-// Position of key kappa (0..63 in a tile) inside a V^T row: bits 2 and 3 of
-// the key index trade places.  The score accumulator of lane half h holds,
-// for each 16-key MFMA chunk, keys {8j + 4h + r}; with this permutation those
-// eight keys sit contiguously at 8h + 4j + r, so one 16-byte LDS read gives
-// the matching V^T operand.
-__device__ __forceinline__ int vt_pos(int kappa)
-{
-    return (kappa & ~0xC) | ((kappa & 4) << 1) | ((kappa & 8) >> 1);
-}
 
 __device__ __forceinline__ void map_workgroup(int L, const PrefillArgs &a, int n_qtiles,
                                               int &b, int &hq, int &qt)
@@ -91,18 +96,21 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
 {
-    using SM = Smem<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SM::stage];
+    using T = Tile<D>;
+    __shared__ __attribute__((aligned(1024))) uint16_t k_st0[T::elems];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_st0[T::elems];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_st1[T::elems];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_st1[T::elems];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, h = lane >> 5;
 
     int b, hq, qt;
     map_workgroup(blockIdx.x, a, n_qtiles, b, hq, qt);
     const int G = a.Hq / a.Hkv, hk = hq / G;
     const int i0 = qt * kBR;
-    const int q0 = i0 + wave * 32;      // first query row of this wave
+    const int q0 = i0 + wave * 32;      // first query row of this wave (uniform)
     const int my_q = q0 + l32;          // query row of this lane
     const int diag = a.Sk - a.Sq;       // key j visible to row i iff j <= i + diag
 
@@ -110,72 +118,76 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
     if (CAUSAL) kend = min(a.Sk, min(a.Sq, i0 + kBR) + diag);
     const int ntiles = kend > 0 ? (kend + kBC - 1) / kBC : 0;
 
-    const uint16_t *__restrict__ qg = static_cast<const uint16_t *>(a.q);
-    const uint16_t *__restrict__ kg = static_cast<const uint16_t *>(a.k);
-    const uint16_t *__restrict__ vg = static_cast<const uint16_t *>(a.v);
+    // Exponent scale c = scale * log2(e), made non-negative by flipping the
+    // sign of Q (exact in bf16) when the caller's scale is negative.
+    const bool neg = a.scale_log2 < 0.f;
+    const float c = neg ? -a.scale_log2 : a.scale_log2;
 
     // Q^T operand of S^T = K Q^T: lane (h, l32) holds q[my_q][16ks + 8h .. +8].
     u32x4_t qf[D / 16];
     {
-        const size_t row = ((size_t)b * a.Sq + my_q) * a.Hq + hq;
+        const uint16_t *qg = static_cast<const uint16_t *>(a.q);
+        const size_t row = ((size_t)b * a.Sq + min(my_q, a.Sq - 1)) * a.Hq + hq;
         const uint16_t *qp = qg + row * D + 8 * h;
+        const uint32_t flip = neg ? 0x80008000u : 0u;
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            qf[ks] = my_q < a.Sq ? *reinterpret_cast<const u32x4_t *>(qp + 16 * ks) : u32x4_t{0, 0, 0, 0};
+        for (int ks = 0; ks < D / 16; ++ks) {
+            u32x4_t x = *reinterpret_cast<const u32x4_t *>(qp + 16 * ks);
+            x ^= flip;
+            qf[ks] = my_q < a.Sq ? x : u32x4_t{0, 0, 0, 0};
+        }
     }
 
-    const size_t kv_rs = (size_t)a.Hkv * D;         // elements between consecutive keys
-    const uint16_t *kbase = kg + (size_t)b * a.Sk * kv_rs + (size_t)hk * D;
-    const uint16_t *vbase = vg + (size_t)b * a.Sk * kv_rs + (size_t)hk * D;
+    // ---- K/V streaming: buffer loads that write LDS directly ------------
+    const uint32_t row_bytes = (uint32_t)(a.Hkv * D * 2);
+    const size_t head_off = ((size_t)b * a.Sk * a.Hkv + hk) * D;      // elements
+    const char *kbase = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k) + head_off);
+    const char *vbase = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.v) + head_off);
+    // Bytes from this head's first key to the end of its last key row.
+    const uint32_t span = a.Sk > 0 ? (uint32_t)(((size_t)(a.Sk - 1) * a.Hkv * D + D) * 2) : 0u;
 
-    // ---- K/V tile staging: global -> registers -> LDS ------------------
-    u32x4_t kreg[SM::kChunks];
-    u32x4_t vreg[4];
-    const bool v_loader = tid < 16 * (D / 8);       // (key quad, 8-wide d chunk) items
-    const int v_kq = tid & 15, v_dc = tid >> 4;
+    // Per-lane source offsets (bytes, relative to the tile's first key) of the
+    // 16-byte chunks this lane's LDS-direct loads deliver: load i of wave w
+    // fills LDS chunk slots (w * loads + i) * 64 + lane.
+    uint32_t src_off[T::loads_per_wave];
+#pragma unroll
+    for (int i = 0; i < T::loads_per_wave; ++i) {
+        const int slot = (wave * T::loads_per_wave + i) * 64 + lane;
+        const int r = slot / T::cpr, p = slot % T::cpr;
+        const int cl = T::swz(r, p);                      // swz is an involution
+        src_off[i] = (uint32_t)r * row_bytes + (uint32_t)cl * 16u;
+    }
 
-    auto load_tile = [&](int j) {
-        const int kv0 = j * kBC;
+    auto issue_tile = [&](int j, uint16_t *ks, uint16_t *vs) __attribute__((always_inline)) {
+        const uint32_t start = (uint32_t)(j * kBC) * row_bytes;
+        const uint32_t left = span > start ? span - start : 0u;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + start, left);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + start, left);
 #pragma unroll
-        for (int i = 0; i < SM::kChunks; ++i) {
-            const int c = tid + kThreads * i;
-            const int row = c / (D / 8), col = c % (D / 8);
-            const int key = kv0 + row;
-            kreg[i] = key < a.Sk ? *reinterpret_cast<const u32x4_t *>(kbase + key * kv_rs + col * 8)
-                                 : u32x4_t{0, 0, 0, 0};
-        }
-        if (v_loader) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = kv0 + 4 * v_kq + r;
-                vreg[r] = key < a.Sk ? *reinterpret_cast<const u32x4_t *>(vbase + key * kv_rs + v_dc * 8)
-                                     : u32x4_t{0, 0, 0, 0};
-            }
+        for (int i = 0; i < T::loads_per_wave; ++i) {
+            const int chunk0 = (wave * T::loads_per_wave + i) * 64;      // uniform
+            buffer_load_lds16(rk, ks + chunk0 * 8, src_off[i]);
+            buffer_load_lds16(rv, vs + chunk0 * 8, src_off[i]);
         }
     };
 
-    auto store_tile = [&](int stage) {
-        uint16_t *ks = smem + stage * SM::stage;
-        uint16_t *vs = ks + SM::kElems;
+    // ---- per-lane LDS read offsets (elements) --------------------------------
+    // K operand (S^T A operand): row l32 (+32 kb), chunk 2 kk + h.
+    int k_rd[D / 16];
 #pragma unroll
-        for (int i = 0; i < SM::kChunks; ++i) {
-            const int c = tid + kThreads * i;
-            const int row = c / (D / 8), col = c % (D / 8);
-            *reinterpret_cast<u32x4_t *>(ks + row * SM::kPitch + col * 8) = kreg[i];
-        }
-        if (v_loader) {
-            // vreg[r] holds V[4kq + r][8dc .. 8dc+7]; write V^T rows 8dc .. 8dc+7,
-            // four consecutive keys (8 bytes) per row.
-            const int pos = vt_pos(4 * v_kq);
+    for (int kk = 0; kk < D / 16; ++kk) k_rd[kk] = l32 * D + T::swz(l32, 2 * kk + h) * 8;
+    // V^T operand via transpose reads: within 16-lane group (hh, dh), source
+    // lane s points at key row 4 hh + 8 t + s/4 and d = 32 db + 16 dh + 4 (s % 4).
+    const int s16 = lane & 15, g16 = lane >> 4, hh = g16 >> 1, dh = g16 & 1;
+    int v_rd[2][D / 32];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x2_t lo = {pack_lo16(vreg[0][i], vreg[1][i]), pack_lo16(vreg[2][i], vreg[3][i])};
-                const u32x2_t hi = {pack_hi16(vreg[0][i], vreg[1][i]), pack_hi16(vreg[2][i], vreg[3][i])};
-                *reinterpret_cast<u32x2_t *>(vs + (8 * v_dc + 2 * i) * SM::vPitch + pos) = lo;
-                *reinterpret_cast<u32x2_t *>(vs + (8 * v_dc + 2 * i + 1) * SM::vPitch + pos) = hi;
-            }
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const int r = 4 * hh + 8 * t + (s16 >> 2);
+            const int d = 32 * db + 16 * dh + 4 * (s16 & 3);
+            v_rd[t][db] = r * D + T::swz(r, d >> 3) * 8 + (d & 7);
         }
-    };
 
     // ---- per-lane softmax state and output accumulator ----------------
     f32x16_t oacc[D / 32];
@@ -185,62 +197,45 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
         for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
     float m = kNegInf;      // exponent reference (log2 domain) of this row
     float lsum = 0.f;       // this lane's share of the row sum
+    const f32x16_t zero16 = {};
 
-    if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
-
-    for (int j = 0; j < ntiles; ++j) {
-        if (j + 1 < ntiles) load_tile(j + 1);
-
-        const uint16_t *ks = smem + (j & 1) * SM::stage;
-        const uint16_t *vs = ks + SM::kElems;
+    auto compute_tile = [&](const uint16_t *ks, const uint16_t *vs, int j, auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
         const int kv0 = j * kBC;
-
-        // Which 32-key halves of the tile can this wave see at all?
-        bool blk_live[2];
+        bool live[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int kstart = kv0 + 32 * kb;
-            blk_live[kb] = kstart < a.Sk && (!CAUSAL || kstart <= q0 + 31 + diag);
+            live[kb] = !MASKED || (kstart < a.Sk && (!CAUSAL || kstart <= q0 + 31 + diag));
         }
-
-        // S^T = K Q^T for the live halves.
+        // S^T = K Q^T
         f32x16_t s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = zero16;
+            if (live[kb]) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-            if (blk_live[kb]) {
-                const uint16_t *kr = ks + (32 * kb + l32) * SM::kPitch + 8 * h;
-#pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk)
-                    s[kb] = mfma_32x32x16_bf16(*reinterpret_cast<const u32x4_t *>(kr + 16 * kk), qf[kk], s[kb]);
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    const u32x4_t kop = *reinterpret_cast<const u32x4_t *>(ks + k_rd[kk] + 32 * kb * D);
+                    s[kb] = mfma_32x32x16_bf16(kop, qf[kk], kk == 0 ? zero16 : s[kb]);
+                }
             }
         }
-
-        // Scale into the exp2 domain and mask where some key may be invisible.
-        const bool need_mask = (kv0 + kBC > a.Sk) || (CAUSAL && kv0 + kBC - 1 > q0 + diag);
-        float mx = kNegInf;
+        // Row max of the raw scores (c >= 0, so scaling preserves order).
+        float mraw = kNegInf;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                float t = s[kb][v] * a.scale_log2;
-                if (need_mask) {
+                if constexpr (MASKED) {
                     const int key = kv0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
                     const bool vis = key < a.Sk && (!CAUSAL || key <= my_q + diag);
-                    t = vis ? t : kNegInf;
+                    s[kb][v] = vis ? s[kb][v] : kNegInf;
                 }
-                s[kb][v] = t;
-                mx = fmaxf(mx, t);
+                mraw = fmaxf(mraw, s[kb][v]);
             }
-        }
-        mx = pair_max_halves(mx);
-
-        // Online softmax with lazy rescaling of the exponent reference.
+        mraw = pair_max_halves(mraw);
+        const float mx = mraw == kNegInf ? kNegInf : mraw * c;
         const float m_new = fmaxf(m, mx);
         const bool grow = m_new > m + 8.0f;
         if (wave_any(grow)) {
@@ -248,45 +243,62 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
             m = grow ? m_new : m;
             lsum *= alpha;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
         }
-        const float mref = (m == kNegInf) ? 0.f : m;
-
-        // P = 2^(t - m), row-sum share, pack to bf16 as the PV B operand.
+        const float nm = (m == kNegInf) ? 0.f : -m;
+        // P = 2^(s c - m) -> bf16 pairs; the row sum adds the rounded values.
         u32x4_t pk[2][2];
-        float rs = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
+            for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float p0 = exp2_fast(s[kb][8 * c + 2 * e] - mref);
-                    const float p1 = exp2_fast(s[kb][8 * c + 2 * e + 1] - mref);
-                    rs += p0 + p1;
-                    pk[kb][c][e] = pack_bf16x2(p0, p1);
+                    float x0 = __builtin_fmaf(s[kb][8 * cc + 2 * e], c, nm);
+                    float x1 = __builtin_fmaf(s[kb][8 * cc + 2 * e + 1], c, nm);
+                    if constexpr (MASKED) {
+                        x0 = s[kb][8 * cc + 2 * e] == kNegInf ? kNegInf : x0;
+                        x1 = s[kb][8 * cc + 2 * e + 1] == kNegInf ? kNegInf : x1;
+                    }
+                    const float p0 = exp2_fast(x0), p1 = exp2_fast(x1);
+                    pk[kb][cc][e] = pack_bf16x2(p0, p1);
+                    lsum += p0 + p1;
                 }
-            }
-        }
-        lsum += rs;
-
         // O^T += V^T P^T over the live halves.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            if (!blk_live[kb]) continue;
+            if (!live[kb]) continue;
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const uint16_t *vr = vs + l32 * SM::vPitch + 32 * kb + 16 * c + 8 * h;
+            for (int cc = 0; cc < 2; ++cc) {
+                const int kbase_el = (32 * kb + 16 * cc) * D;
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-                    oacc[db] = mfma_32x32x16_bf16(*reinterpret_cast<const u32x4_t *>(vr + 32 * db * SM::vPitch),
-                                                  pk[kb][c], oacc[db]);
+                for (int db = 0; db < D / 32; ++db) {
+                    const u32x2_t lo = lds_read_tr16(vs + v_rd[0][db] + kbase_el);
+                    const u32x2_t hi = lds_read_tr16(vs + v_rd[1][db] + kbase_el);
+                    const u32x4_t vop = {lo[0], lo[1], hi[0], hi[1]};
+                    oacc[db] = mfma_32x32x16_bf16(vop, pk[kb][cc], oacc[db]);
+                }
             }
         }
+    };
 
-        if (j + 1 < ntiles) store_tile((j + 1) & 1);
+    // Tiles before `first_masked` are fully visible to every row of this wave.
+    int first_masked = a.Sk / kBC;                       // full tiles inside the sequence
+    if (CAUSAL) first_masked = min(first_masked, max(0, (q0 + diag + 1) / kBC));
+    auto run_tile = [&](const uint16_t *ks, const uint16_t *vs, int j) __attribute__((always_inline)) {
+        if (j >= first_masked) compute_tile(ks, vs, j, std::true_type{});
+        else compute_tile(ks, vs, j, std::false_type{});
+    };
+
+    if (ntiles > 0) issue_tile(0, k_st0, v_st0);
+    __syncthreads();
+    for (int j = 0; j < ntiles; j += 2) {
+        if (j + 1 < ntiles) issue_tile(j + 1, k_st1, v_st1);
+        run_tile(k_st0, v_st0, j);
+        __syncthreads();
+        if (j + 1 >= ntiles) break;
+        if (j + 2 < ntiles) issue_tile(j + 2, k_st0, v_st0);
+        run_tile(k_st1, v_st1, j + 1);
         __syncthreads();
     }
 

@@ -154,3 +154,14 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         afa.prefill(q, q[:, :, :1].contiguous(), q[:, :, :1].contiguous())
+
+
+def test_every_kernel_launch_stub_is_defined():
+    # A kernel whose body the host pass cannot compile (for example a device
+    # builtin called directly from a lambda) silently loses its launch stub;
+    # the library then fails to load with an undefined symbol.
+    import subprocess
+    out = subprocess.run(["nm", "-u", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    missing = [line for line in out.splitlines() if "__device_stub__" in line]
+    assert not missing, missing
