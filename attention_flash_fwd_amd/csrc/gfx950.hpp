@@ -104,11 +104,36 @@ __device__ __forceinline__ void *uniform_ptr(const void *p)
     return reinterpret_cast<void *>(lo | (hi << 32));
 }
 
+// Returns x unchanged but hides its value from the optimiser, so that
+// per-lane address arithmetic derived from it stays where it is written
+// instead of being hoisted out of a loop into long-lived registers.
+__device__ __forceinline__ int opaque(int x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // Raw buffer descriptor over [base, base + bytes): loads at offsets past the
 // end return zero (word 3 = 0x00020000, the gfx9 raw-buffer format).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(base), (short)0, (int)uniform_u32(bytes), 0x00020000);
+}
+
+// 16 bytes per lane from buffer offset voff (zero past the end of the buffer).
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
+{
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
+// but leaves its global loads in flight (a full __syncthreads() fence would
+// also wait for every outstanding global load).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // 16 bytes per lane from buffer offset voff straight into LDS: the wave's 64

@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
 PEAK_HBM_BPS = 8.0e12         # MI355X HBM3E
+COPY_BYTES = 1 << 30          # calibration copy (profiling runs only)
 METRIC = "prefill attn TFLOP/s + decode KV GB/s, % of MI355X bf16/HBM peak"
 
 
@@ -40,7 +41,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--parts", default="prefill,decode_b64,decode_128k",
-                   help="comma-separated subset (for profiling runs)")
+                   help="comma-separated subset (for profiling runs); 'copy' adds a plain "
+                        "1 GiB device-to-device copy that calibrates the HBM byte counters")
     return p.parse_args()
 
 
@@ -63,21 +65,27 @@ def source_digest(paths):
     return h.hexdigest()[:16]
 
 
-PREFILL_SOURCES = ["attention_flash_fwd_amd/csrc/prefill_bf16.hip",
-                   "attention_flash_fwd_amd/csrc/gfx950.hpp"]
+KERNEL_SOURCES = {
+    "prefill": ["attention_flash_fwd_amd/csrc/prefill_bf16.hip", "attention_flash_fwd_amd/csrc/gfx950.hpp",
+                "attention_flash_fwd_amd/csrc/kernels.hpp"],
+    "decode": ["attention_flash_fwd_amd/csrc/decode.hip", "attention_flash_fwd_amd/csrc/gfx950.hpp",
+               "attention_flash_fwd_amd/csrc/kernels.hpp"],
+}
+TRAFFIC_KEYS = {"prefill": "prefill_8k", "decode_b64": "decode_b64", "decode_128k": "decode_128k"}
 
 
-def load_traffic(kernel_digest):
-    """HBM bytes per prefill launch from the committed rocprofv3 counter runs,
-    if they were taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "prefill_8k_traffic.json")
+def load_traffic(part, kernel_digest):
+    """HBM bytes (read + write) per call of `part` from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, if they were taken on the current
+    kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f)
-    if rec.get("kernel_digest") != kernel_digest:
+        rec = json.load(f).get(TRAFFIC_KEYS[part])
+    if rec is None or rec.get("source_digest") != kernel_digest:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes")
 
 
 def cpu_baseline(parts, pf_cfg, pf_in, dec_parts):
@@ -97,11 +105,12 @@ def cpu_baseline(parts, pf_cfg, pf_in, dec_parts):
         q, k, v = pf_in
         rng = np.random.default_rng(0)
         B, S, Hq, D = q.shape
-        n_rows = 4096
+        n_rows = 131072
         rows = [(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(S))) for _ in range(n_rows)]
         qn = q.float().cpu().numpy()
         kn = k.float().cpu().numpy()
         vn = v.float().cpu().numpy()
+        print(f"cpu baseline: prefill, {n_rows} rows on {threads} threads", file=sys.stderr, flush=True)
         t0 = time.perf_counter()
         oracle.attention_rows(qn, kn, vn, True, pf_cfg.scale, rows, nthreads=threads)
         dt = time.perf_counter() - t0
@@ -112,7 +121,7 @@ def cpu_baseline(parts, pf_cfg, pf_in, dec_parts):
         detail["prefill_gflops"] = rate / 1e9
         detail["prefill_sample"] = f"{n_rows} random query rows of all {B * Hq} heads"
     for name, (inp, Hq, scale, nbytes) in dec_parts.items():
-        n_seq = 2
+        n_seq = 16
         seqs = list(range(min(n_seq, inp.batch)))
         qn = inp.q.float().cpu().numpy()
         ks, vs, byts = [], [], 0
@@ -121,6 +130,7 @@ def cpu_baseline(parts, pf_cfg, pf_in, dec_parts):
             ks.append(kb.float().numpy())
             vs.append(vb.float().numpy())
             byts += 2 * kb.numel() * 2
+        print(f"cpu baseline: {name}, {len(seqs)} sequences", file=sys.stderr, flush=True)
         t0 = time.perf_counter()
         oracle.decode(qn[seqs], ks, vs, scale, nthreads=threads)
         dt = time.perf_counter() - t0
@@ -180,6 +190,10 @@ def main():
                          num_splits=cfg.num_splits, scale=cfg.scale, out=o, lse_out=lse, workspace=ws)
 
     runners = []
+    if "copy" in parts:
+        copy_src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+        copy_dst = torch.empty_like(copy_src)
+        runners.append(("copy", lambda: copy_dst.copy_(copy_src)))
     if pf_in is not None:
         runners.append(("prefill", run_prefill))
     for name in dec:
@@ -227,22 +241,27 @@ def main():
         out_parts[name] = {"workload": cfg.name, "ms": part_ms[name], "gbps": gbps,
                            "frac_of_peak": gbps * 1e9 / PEAK_HBM_BPS, "bytes": nb,
                            "num_splits": cfg.num_splits, "sum_ctx": sum(inp.ctx)}
-    value = 100.0 * sol_ms / ms_per_step
+    if "copy" in part_ms:
+        out_parts["copy"] = {"workload": f"device copy of {COPY_BYTES} B", "ms": part_ms["copy"],
+                             "gbps": 2 * COPY_BYTES / (part_ms["copy"] * 1e-3) / 1e9}
+    path_ms = ms_per_step - part_ms.get("copy", 0.0)
+    value = 100.0 * sol_ms / path_ms if sol_ms > 0 and path_ms > 0 else None
 
     roofline = None
     if pf_in is not None:
-        digest = source_digest(PREFILL_SOURCES)
+        digest = source_digest(KERNEL_SOURCES["prefill"])
         achieved = out_parts["prefill"]["tflops"]
         roofline = {"bound": "mfma", "kernel": "prefill_bf16_kernel<128,true>",
                     "achieved": achieved, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
-                    "frac": achieved * 1e12 / PEAK_BF16_FLOPS, "traffic": load_traffic(digest),
+                    "frac": achieved * 1e12 / PEAK_BF16_FLOPS, "traffic": load_traffic("prefill", digest),
                     "per_launch_flops": pf_cfg.flops(), "avg_launch_ms": part_ms["prefill"],
                     "kernel_digest": digest}
     decode_roofline = {
         name: {"bound": "hbm", "achieved": p["gbps"], "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                "frac": p["frac_of_peak"], "per_launch_bytes": p["bytes"], "avg_launch_ms": p["ms"],
+               "traffic": load_traffic(name, source_digest(KERNEL_SOURCES["decode"])),
                "note": "split + combine kernels of one attn_decode_paged call"}
-        for name, p in out_parts.items() if name != "prefill"}
+        for name, p in out_parts.items() if name.startswith("decode")}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -250,7 +269,7 @@ def main():
                      for name, (cfg, inp, ws, o, lse) in dec.items()}
         cpu = cpu_baseline(parts, pf_cfg, pf_in, dec_parts)
 
-    workload = " + ".join(out_parts[p]["workload"] for p in out_parts)
+    workload = " + ".join(out_parts[p]["workload"] for p in out_parts if p != "copy")
     rec = {
         "metric": METRIC,
         "value": value,
