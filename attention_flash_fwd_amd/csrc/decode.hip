@@ -6,22 +6,29 @@
 // fp32; chenyy20.com "抱infra脚", section Paged Attention: fixed-size blocks
 // reached through a block table).
 //
-// Kernel 1, decode_split: one workgroup per (chunk, KV head, sequence).  The
-//   G = Hq / Hkv query heads that share the KV head are packed as the columns
-//   of 16x16x32 bf16 MFMAs, so each K/V byte is read from HBM once for all of
-//   them.  The four waves of the workgroup take turns over pairs of 16-token
-//   cache blocks; each wave keeps its own running max / sum and its partial
-//   output, with the next pair's K/V loads in flight while the current pair
-//   is computed.  K goes straight from global memory into MFMA A operands;
-//   V is transposed through a wave-private LDS slab.  Tokens past the chunk
-//   end are never read (their operands are zero), so unused cache slots may
-//   hold anything.  The four wave partials are merged in LDS and the chunk's
+// Kernel 1, decode_split: one workgroup of four waves per (chunk, KV head,
+//   sequence).  The G = Hq / Hkv query heads that share the KV head are the
+//   columns of the matrix-core products, so each K/V byte is read from HBM
+//   once for all of them.  The chunk's 16-token cache blocks are dealt
+//   round-robin to the waves.  Each wave streams its blocks with LDS-direct
+//   buffer loads into a private two-slot ring (the next block lands while
+//   the current one is computed) and keeps its own running max, running sum
+//   and partial output.  Per block:
+//     S^T (16 tokens x 16 heads)  = K Q^T        4 x 16x16x32 bf16 MFMA
+//     P = 2^(S - m), lazy rescale of (l, O) when the max grows by > 2^8
+//     O^T (D x 16 heads)         += V^T P^T      D/16 x 16x16x16 bf16 MFMA
+//   The score accumulator of a lane (4 tokens of one head) is exactly the
+//   B operand the 16x16x16 product wants, and the V^T operand comes from one
+//   transposing LDS read per 16 rows of d.  Cache slots past the chunk end
+//   are never fetched (their buffer offsets fall outside the block and read
+//   as zero).  The four wave partials are merged in LDS and the chunk's
 //   normalised output and log-sum-exp are written as fp32.
-// Kernel 2, decode_combine: one wave per (sequence, query head) merges the
-//   chunk partials: M = max lse_s, w_s = e^(lse_s - M), O = sum w_s O_s / sum w_s,
-//   lse = M + ln sum w_s; O rounded to bf16.
+// Kernel 2, decode_combine: one workgroup per (sequence, query head) merges
+//   the chunk partials: M = max lse_s, w_s = e^(lse_s - M),
+//   O = sum w_s O_s / sum w_s, lse = M + ln sum w_s; O rounded to bf16.
 #include "gfx950.hpp"
 #include "kernels.hpp"
+#include "../../include/attn.h"
 
 namespace attn {
 namespace {
@@ -29,23 +36,131 @@ namespace {
 constexpr int kBS = 16;         // tokens per cache block
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr uint32_t kOutside = 0x80000000u;   // buffer offset past any block: reads zero
 
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_16x16x16_bf16(u32x2_t a, u32x2_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, a),
+                                                     __builtin_bit_cast(bf16x4_t, b), c, 0, 0, 0);
+}
+
+// One cache block of one KV head in LDS: 16 token rows of D bf16.  16-byte
+// chunk c of row r holds global chunk c ^ swz(r), which keeps both the
+// row-wise K reads and the transposing V reads free of bank conflicts.
 template <int D>
-struct DecodeSmem {
-    static constexpr int pitch = D + 8;                 // V row pitch (bf16)
-    static constexpr int slab = 2 * kBS * pitch;        // two blocks, per wave (bf16 elements)
-    static constexpr int vbytes = kWaves * slab * 2;
-    static constexpr int cbytes = kWaves * (16 * D + 32) * 4;   // partial O + m + l per wave
-    static constexpr int bytes = vbytes > cbytes ? vbytes : cbytes;
+struct Geom {
+    static constexpr int row_bytes = 2 * D;
+    static constexpr int rows_per_load = 1024 / row_bytes;   // rows one wave-wide DMA fills
+    static constexpr int loads = kBS / rows_per_load;        // DMAs per block of K (or V)
+    static constexpr int slot_bytes = kBS * row_bytes;
+    __device__ static __forceinline__ int swz(int r)
+    {
+        return D == 128 ? (((r << 1) | (r >> 3)) & 15) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+    }
 };
 
+// Per-wave state of the split kernel.
 template <int D>
-__global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a)
-{
-    using SM = DecodeSmem<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SM::bytes];
+struct WaveState {
+    u32x4_t qf[D / 32];         // Q^T operand: head l16, d = 32 kk + 8 g .. +8
+    f32x4_t o[D / 16];          // O^T: head l16, d = 16 db + 4 g + v
+    float m, l;
+};
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Queue the K and V of one block into a slot.  `valid` rows (tokens) are
+// fetched, the rest read as zero; voff[i] is this lane's offset in the block
+// for its row of DMA i.
+template <int D>
+__device__ __forceinline__ void issue_block(const uint16_t *kc, const uint16_t *vc, long long phys,
+                                            uint32_t blk_bytes, int valid, const uint32_t (&voff)[Geom<D>::loads],
+                                            int lane, uint8_t *ks, uint8_t *vs)
+{
+    using Gm = Geom<D>;
+    const char *kb = reinterpret_cast<const char *>(kc) + phys * blk_bytes;
+    const char *vb = reinterpret_cast<const char *>(vc) + phys * blk_bytes;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, blk_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, blk_bytes);
+    const int row0 = lane / (Gm::row_bytes / 16);
+#pragma unroll
+    for (int i = 0; i < Gm::loads; ++i) {
+        const uint32_t off = (i * Gm::rows_per_load + row0 < valid) ? voff[i] : kOutside;
+        buffer_load_lds16(rk, ks + 1024 * i, off);
+        buffer_load_lds16(rv, vs + 1024 * i, off);
+    }
+}
+
+// One block from a slot: scores, online softmax, PV.
+template <int D>
+__device__ __forceinline__ void compute_block(const uint8_t *ks, const uint8_t *vs, int valid,
+                                              float scale_log2, int l16, int g, WaveState<D> &w)
+{
+    using Gm = Geom<D>;
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    {
+        const uint8_t *row = ks + l16 * Gm::row_bytes;
+        const int sw = Gm::swz(l16);
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(row + (((4 * kk + g) ^ sw) << 4));
+            s = mfma_16x16x32_bf16(kf, w.qf[kk], s);
+        }
+    }
+    // Lane (g, l16) holds tokens 4 g + v of head l16.
+    float mx = kNegInf;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const float t = (4 * g + v < valid) ? s[v] * scale_log2 : kNegInf;
+        s[v] = t;
+        mx = fmaxf(mx, t);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(w.m, mx);
+    const bool grow = m_new > w.m + 8.0f;
+    if (wave_any(grow)) {
+        const float alpha = grow ? exp2_fast(w.m - m_new) : 1.0f;
+        w.m = grow ? m_new : w.m;
+        w.l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) w.o[db] *= alpha;
+    }
+    const float mref = (w.m == kNegInf) ? 0.f : w.m;
+    float p[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        p[v] = exp2_fast(s[v] - mref);
+        w.l += p[v];
+    }
+    const u32x2_t pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+
+    // V^T operand: lane (g, i) receives V[4 g + e][16 db + i], e = 0..3, from
+    // the rows 4 g + l16 / 4 read by its group.
+    const int vr = 4 * g + (l16 >> 2);
+    const uint8_t *vrow = vs + vr * Gm::row_bytes + ((l16 & 1) << 3);
+    const int vsw = Gm::swz(vr);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+        const int chunk = 2 * db + ((l16 & 3) >> 1);
+        const u32x2_t vt = lds_read_tr16(reinterpret_cast<const uint16_t *>(vrow + ((chunk ^ vsw) << 4)));
+        w.o[db] = mfma_16x16x16_bf16(vt, pk, w.o[db]);
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
+{
+    using Gm = Geom<D>;
+    // Two ring slots per wave, K and V each in an array of its own so that the
+    // compiler's wait for a slot's loads does not also wait for the other's.
+    __shared__ __attribute__((aligned(1024))) uint8_t k_s0[kWaves][Gm::slot_bytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_s0[kWaves][Gm::slot_bytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_s1[kWaves][Gm::slot_bytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_s1[kWaves][Gm::slot_bytes];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = (int)uniform_u32(threadIdx.x >> 6);
     const int l16 = lane & 15, g = lane >> 4;
 
     const int split = blockIdx.x % a.splits;
@@ -53,7 +168,9 @@ __global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a)
     const int b = blockIdx.x / (a.splits * a.Hkv);
     const int G = a.Hq / a.Hkv;
 
-    const int ctx = a.ctx_lens[b];
+    // Sequence length through the scalar cache: everything derived from it
+    // (chunk bounds, trip counts) stays wave-uniform.
+    const int ctx = ((const int32_t __attribute__((address_space(4))) *)a.ctx_lens)[b];
     bool bad = ctx < 0 || ctx > a.max_blocks * kBS;
     int t_begin = 0, t_end = 0;
     if (!bad && ctx > 0) {
@@ -64,168 +181,115 @@ __global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a)
     }
     const int blk0 = t_begin / kBS;
     const int nblk = (t_end - t_begin + kBS - 1) / kBS;
-    const int nsteps = (nblk + 1) / 2;                  // pairs of blocks
+    // This wave's blocks: chunk blocks wave, wave + 4, ...
+    const int nmine = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
 
-    // Q^T operand: lane (g, l16) holds q[head l16][32 kk + 8 g .. +8]; heads past G are 0.
-    u32x4_t qf[D / 32];
+    WaveState<D> w;
     {
+        // Columns past G read head G - 1 and are zeroed (no branch around the load).
         const bool hv = l16 < G;
-        const uint16_t *qp = a.q + ((size_t)b * a.Hq + hk * G + (hv ? l16 : 0)) * D + 8 * g;
+        const uint16_t *qp = a.q + ((size_t)b * a.Hq + hk * G + min(l16, G - 1)) * D + 8 * g;
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-            qf[kk] = hv ? *reinterpret_cast<const u32x4_t *>(qp + 32 * kk) : u32x4_t{0, 0, 0, 0};
+        for (int kk = 0; kk < D / 32; ++kk) {
+            const u32x4_t x = *reinterpret_cast<const u32x4_t *>(qp + 32 * kk);
+            w.qf[kk] = hv ? x : u32x4_t{0, 0, 0, 0};
+        }
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) w.o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    w.m = kNegInf;
+    w.l = 0.f;
+
+    // Physical block ids come through the scalar cache (the table is read-only
+    // here), one block ahead of their use, so that the loop issues no vector
+    // loads besides the K/V streams and every wait for a slot is exact.
+    const int32_t __attribute__((address_space(4))) *tb =
+        (const int32_t __attribute__((address_space(4))) *)(a.block_table + (size_t)b * a.max_blocks + blk0 + wave);
+    int phys_next = nmine > 0 ? tb[0] : 0;
+
+    // This lane's offset inside a block for each of its DMAs: row
+    // i * rows_per_load + lane / chunks_per_row, chunk lane % chunks_per_row
+    // filled from global chunk (lane % chunks_per_row) ^ swz(row).
+    const uint32_t blk_bytes = (uint32_t)(kBS * a.Hkv * Gm::row_bytes);
+    uint32_t voff[Gm::loads];
+    {
+        constexpr int cpr = Gm::row_bytes / 16;
+#pragma unroll
+        for (int i = 0; i < Gm::loads; ++i) {
+            const int r = i * Gm::rows_per_load + lane / cpr;
+            const int c = (lane % cpr) ^ Gm::swz(r);
+            voff[i] = (uint32_t)(r * a.Hkv * Gm::row_bytes + hk * Gm::row_bytes + 16 * c);
+        }
     }
 
-    const size_t tok_rs = (size_t)a.Hkv * D;            // elements between tokens of a block
-    const size_t blk_rs = (size_t)kBS * tok_rs;         // elements between blocks
-    const int32_t *table = a.block_table + (size_t)b * a.max_blocks;
-
-    // Loads of one step: blocks (blk0 + 2 st, +1); lane (g, l16) fetches token l16's
-    // d-range 32 kk + 8 g .. +8 of K and V for each block.
-    u32x4_t kc[2][D / 32], vc[2][D / 32];
-    auto load_step = [&](int st, u32x4_t (&kr)[2][D / 32], u32x4_t (&vr)[2][D / 32], bool &oob) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int lb = 2 * st + p;                  // block index within the chunk
-            int phys = -1;
-            if (lb < nblk) phys = table[blk0 + lb];
-            const bool in_pool = phys >= 0 && phys < a.num_blocks;
-            if (lb < nblk && !in_pool) oob = true;
-            const int tok = (blk0 + lb) * kBS + l16;
-            const bool live = lb < nblk && in_pool && tok < t_end;
-            const size_t base = (size_t)(in_pool ? phys : 0) * blk_rs + (size_t)l16 * tok_rs + (size_t)hk * D + 8 * g;
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                kr[p][kk] = live ? *reinterpret_cast<const u32x4_t *>(a.k_cache + base + 32 * kk) : u32x4_t{0, 0, 0, 0};
-                vr[p][kk] = live ? *reinterpret_cast<const u32x4_t *>(a.v_cache + base + 32 * kk) : u32x4_t{0, 0, 0, 0};
+    // Issue block j of this wave into a slot (j past the end: nothing fetched).
+    auto issue = [&](int j, uint8_t *ks, uint8_t *vs) __attribute__((always_inline)) {
+        long long phys = 0;
+        int valid = 0;
+        if (j < nmine) {
+            const int p = phys_next;
+            phys_next = j + 1 < nmine ? tb[kWaves * (j + 1)] : 0;
+            const int tok0 = (blk0 + wave + kWaves * j) * kBS;
+            if (p < 0 || p >= a.num_blocks) {
+                bad = true;
+            } else {
+                phys = p;
+                valid = min(kBS, t_end - tok0);
             }
         }
+        issue_block<D>(a.k_cache, a.v_cache, phys, blk_bytes, valid, voff, lane, ks, vs);
+    };
+    auto valid_rows = [&](int j) __attribute__((always_inline)) {
+        return min(kBS, t_end - (blk0 + wave + kWaves * j) * kBS);
     };
 
-    f32x4_t oacc[D / 16];
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m = kNegInf, lsum = 0.f;
-
-    uint16_t *slab = reinterpret_cast<uint16_t *>(smem_raw) + wave * SM::slab;
-
-    int st = wave;
-    if (st < nsteps) load_step(st, kc, vc, bad);
-    for (; st < nsteps; st += kWaves) {
-        u32x4_t kn[2][D / 32], vn[2][D / 32];
-        const bool more = st + kWaves < nsteps;
-        if (more) load_step(st + kWaves, kn, vn, bad);
-
-        // S^T (16 tokens x 16 heads) per block.
-        f32x4_t s[2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            s[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) s[p] = mfma_16x16x32_bf16(kc[p][kk], qf[kk], s[p]);
-        }
-        // Lane (g, l16) holds tokens 4g + v of each block for head l16.
-        float mx = kNegInf;
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int tok = (blk0 + 2 * st + p) * kBS + 4 * g + v;
-                const float t = tok < t_end ? s[p][v] * a.scale_log2 : kNegInf;
-                s[p][v] = t;
-                mx = fmaxf(mx, t);
-            }
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m, mx);
-        const bool grow = m_new > m + 8.0f;
-        if (wave_any(grow)) {
-            const float alpha = grow ? exp2_fast(m - m_new) : 1.0f;
-            m = grow ? m_new : m;
-            lsum *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
-        }
-        const float mref = (m == kNegInf) ? 0.f : m;
-        float pv[2][4];
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                pv[p][v] = exp2_fast(s[p][v] - mref);
-                lsum += pv[p][v];
-            }
-        // P^T operand: k-slots 0..3 = block 0 tokens 4g..4g+3, 4..7 = block 1.
-        const u32x4_t pk = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
-                            pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
-
-        // V^T operand through LDS: write both blocks row-major, read columns.
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk)
-                *reinterpret_cast<u32x4_t *>(slab + (p * kBS + l16) * SM::pitch + 32 * kk + 8 * g) = vc[p][kk];
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-            const uint16_t *col = slab + 4 * g * SM::pitch + 16 * db + l16;
-            u32x4_t a_op;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int p = e >> 1, r = 2 * (e & 1);
-                const uint32_t x0 = col[(p * kBS + r) * SM::pitch];
-                const uint32_t x1 = col[(p * kBS + r + 1) * SM::pitch];
-                a_op[e] = x0 | (x1 << 16);
-            }
-            oacc[db] = mfma_16x16x32_bf16(a_op, pk, oacc[db]);
-        }
-        __builtin_amdgcn_wave_barrier();
-
-        if (more) {
-#pragma unroll
-            for (int p = 0; p < 2; ++p)
-#pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk) {
-                    kc[p][kk] = kn[p][kk];
-                    vc[p][kk] = vn[p][kk];
-                }
-        }
+    // Every path through the loop issues the same loads in the same order,
+    // so the wait before each slot's reads is exact.
+    issue(0, k_s0[wave], v_s0[wave]);
+    issue(1, k_s1[wave], v_s1[wave]);
+    for (int j = 0; j < nmine; j += 2) {
+        compute_block<D>(k_s0[wave], v_s0[wave], valid_rows(j), a.scale_log2, l16, g, w);
+        issue(j + 2, k_s0[wave], v_s0[wave]);
+        if (j + 1 < nmine)
+            compute_block<D>(k_s1[wave], v_s1[wave], valid_rows(j + 1), a.scale_log2, l16, g, w);
+        issue(j + 3, k_s1[wave], v_s1[wave]);
     }
 
     // Row sums: lanes g = 0..3 of a head hold disjoint tokens.
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
+    w.l += __shfl_xor(w.l, 16);
+    w.l += __shfl_xor(w.l, 32);
 
-    // Merge the four wave partials of this chunk in LDS.
-    __syncthreads();                                    // V slabs are free now
-    float *cm = reinterpret_cast<float *>(smem_raw);    // [wave][16] m, then l, then O [wave][16][D]
-    float *cl = cm + kWaves * 16;
-    float *co = cl + kWaves * 16;
+    // Merge the four wave partials in LDS.  The ring is free once every wave
+    // has drained its loads (the trailing ones past the chunk end fetch
+    // nothing but still write zeros) and passed the barrier.
+    __builtin_amdgcn_s_waitcnt(0);
+    const bool any_bad = __syncthreads_or(bad);
+    float *mo = reinterpret_cast<float *>(wave < 2 ? &k_s0[0][0] : &v_s0[0][0]) + (wave & 1) * 16 * D;
+    float *ml = reinterpret_cast<float *>(&k_s1[0][0]);      // [wave][16] m, then [wave][16] l
     if (g == 0) {
-        cm[wave * 16 + l16] = m;
-        cl[wave * 16 + l16] = lsum;
+        ml[wave * 16 + l16] = w.m;
+        ml[kWaves * 16 + wave * 16 + l16] = w.l;
     }
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) co[(wave * 16 + l16) * D + 16 * db + 4 * g + v] = oacc[db][v];
-    const bool any_bad = __syncthreads_or(bad);
+        *reinterpret_cast<f32x4_t *>(mo + l16 * D + 16 * db + 4 * g) = w.o[db];
+    __syncthreads();
 
-    for (int idx = tid; idx < G * D; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
         const int head = idx / D, d = idx % D;
         float M = kNegInf;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cm[w * 16 + head]);
+        for (int v = 0; v < kWaves; ++v) M = fmaxf(M, ml[v * 16 + head]);
         float L = 0.f, O = 0.f;
         if (M != kNegInf) {
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float mw = cm[w * 16 + head];
-                if (mw == kNegInf) continue;
-                const float sc = exp2_fast(mw - M);
-                L += cl[w * 16 + head] * sc;
-                O += co[(w * 16 + head) * D + d] * sc;
+            for (int v = 0; v < kWaves; ++v) {
+                const float mv = ml[v * 16 + head];
+                if (mv == kNegInf) continue;
+                const float sc = exp2_fast(mv - M);
+                const float *src = reinterpret_cast<const float *>(v < 2 ? &k_s0[0][0] : &v_s0[0][0]) + (v & 1) * 16 * D;
+                L += ml[kWaves * 16 + v * 16 + head] * sc;
+                O += src[head * D + d] * sc;
             }
         }
         const size_t row = ((size_t)b * a.Hq + hk * G + head) * a.splits + split;
@@ -240,47 +304,83 @@ __global__ void __launch_bounds__(kThreads) decode_split_kernel(DecodeArgs a)
     }
 }
 
-// One wave per (sequence, query head).
+// One workgroup per (sequence, query head).  Threads own 4 consecutive d of
+// one split row; the workgroup covers kThreads / (D / 4) splits at a time.
 template <int D>
-__global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a)
+__global__ void __launch_bounds__(kThreads) decode_combine_kernel(DecodeArgs a)
 {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);   // b * Hq + hq
-    if (row >= a.B * a.Hq) return;
-    constexpr int PER = D / 64;                            // d values per lane
-    const float *plse = a.part_lse + (size_t)row * a.splits;
-    const float *po = a.part_o + (size_t)row * a.splits * D;
+    constexpr int TPR = D / 4;                 // threads per split row
+    constexpr int SUB = kThreads / TPR;        // split rows in flight per pass
+    constexpr int PRE = 8;                     // rows per thread loaded before the weights are known
+    __shared__ float wts[ATTN_MAX_SPLITS];
+    __shared__ f32x4_t red[SUB][TPR];
+    __shared__ float stat[3];
 
-    float M = kNegInf;
-    bool nan = false;
-    for (int s = 0; s < a.splits; ++s) {
-        const float x = plse[s];
-        nan |= (x != x);
-        M = fmaxf(M, x);
+    const int row = blockIdx.x;                // b * Hq + hq
+    const int t = threadIdx.x, sub = t / TPR, c = t % TPR;
+    const int S = a.splits;
+    const float *plse = a.part_lse + (size_t)row * S;
+    const f32x4_t *po = reinterpret_cast<const f32x4_t *>(a.part_o + (size_t)row * S * D) + c;
+
+    f32x4_t pre[PRE];
+#pragma unroll
+    for (int i = 0; i < PRE; ++i) {
+        const int s = sub + SUB * i;
+        pre[i] = s < S ? po[(size_t)s * TPR] : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    float acc[PER];
+    for (int s = t; s < S; s += kThreads) wts[s] = plse[s];
+    __syncthreads();
+    if (t < 64) {
+        float M = kNegInf;
+        bool nan = false;
+        for (int s = t; s < S; s += 64) {
+            const float x = wts[s];
+            nan |= (x != x);
+            M = fmaxf(M, x);
+        }
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-    float wsum = 0.f;
-    if (M != kNegInf && !nan) {
-        for (int s = 0; s < a.splits; ++s) {
-            const float x = plse[s];
-            if (x == kNegInf) continue;
-            const float w = exp2_fast((x - M) * kLog2e);
-            wsum += w;
+        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        nan = wave_any(nan);
+        float sum = 0.f;
+        for (int s = t; s < S; s += 64) {
+            const float x = wts[s];
+            const float wv = (M == kNegInf || x == kNegInf) ? 0.f : exp2_fast((x - M) * kLog2e);
+            wts[s] = wv;
+            sum += wv;
+        }
 #pragma unroll
-            for (int i = 0; i < PER; ++i) acc[i] += w * po[(size_t)s * D + lane + 64 * i];
+        for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+        if (t == 0) {
+            stat[0] = M;
+            stat[1] = sum;
+            stat[2] = nan ? 1.f : 0.f;
         }
     }
-    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-    uint16_t *op = a.o + (size_t)row * D;
+    __syncthreads();
+
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const float val = nan ? __builtin_nanf("") : acc[i] * inv;
-        const uint32_t packed = pack_bf16x2(val, 0.f);
-        op[lane + 64 * i] = (uint16_t)(packed & 0xFFFFu);
+    for (int i = 0; i < PRE; ++i) {
+        const int s = sub + SUB * i;
+        if (s < S) acc += wts[s] * pre[i];
     }
-    if (a.lse != nullptr && lane == 0)
+    for (int s = sub + SUB * PRE; s < S; s += SUB) acc += wts[s] * po[(size_t)s * TPR];
+    red[sub][c] = acc;
+    __syncthreads();
+
+    const float M = stat[0], wsum = stat[1];
+    const bool nan = stat[2] != 0.f;
+    if (t < TPR) {
+        f32x4_t o = red[0][t];
+#pragma unroll
+        for (int u = 1; u < SUB; ++u) o += red[u][t];
+        const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+        o *= inv;
+        if (nan) o = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        const u32x2_t packed = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        *reinterpret_cast<u32x2_t *>(a.o + (size_t)row * D + 4 * t) = packed;
+    }
+    if (a.lse != nullptr && t == 0)
         a.lse[row] = nan ? __builtin_nanf("") : (wsum > 0.f ? M + logf(wsum) : kNegInf);
 }
 
@@ -292,8 +392,7 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
     hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)g1), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long long g2 = ((long long)a.B * a.Hq + 3) / 4;
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)g2), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.B * a.Hq)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
