@@ -52,6 +52,10 @@ constexpr int kBC = 64;       // keys per K/V tile
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 
+// An empty volatile asm statement: placed inside a rarely taken branch it
+// keeps the compiler from turning the branch into unconditional arithmetic.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
 template <int D>
 struct Tile {
     static constexpr int cpr = D / 8;                     // 16-byte chunks per row
@@ -199,46 +203,50 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
     float lsum = 0.f;       // this lane's share of the row sum
     const f32x16_t zero16 = {};
 
-    auto compute_tile = [&](const uint16_t *ks, const uint16_t *vs, int j, auto masked_tag) __attribute__((always_inline)) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
+    // Tiles before `first_masked` are fully visible to every row of this wave.
+    int first_masked = a.Sk / kBC;                       // full tiles inside the sequence
+    if (CAUSAL) first_masked = min(first_masked, max(0, (q0 + diag + 1) / kBC));
+
+    // One code path for every tile: masking is a uniform branch around the
+    // few instructions that need it, so the output accumulator keeps its
+    // registers across tiles.
+    auto run_tile = [&](const uint16_t *ks, const uint16_t *vs, int j, auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool masked = decltype(masked_tag)::value;
         const int kv0 = j * kBC;
-        bool live[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int kstart = kv0 + 32 * kb;
-            live[kb] = !MASKED || (kstart < a.Sk && (!CAUSAL || kstart <= q0 + 31 + diag));
-        }
-        // S^T = K Q^T
+        // S^T = K Q^T (both 32-key halves; on diagonal tiles a half may be
+        // fully masked, which the mask below handles)
         f32x16_t s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = zero16;
-            if (live[kb]) {
+            s[kb] = mfma_32x32x16_bf16(*reinterpret_cast<const u32x4_t *>(ks + k_rd[0] + 32 * kb * D), qf[0], zero16);
 #pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) {
-                    const u32x4_t kop = *reinterpret_cast<const u32x4_t *>(ks + k_rd[kk] + 32 * kb * D);
-                    s[kb] = mfma_32x32x16_bf16(kop, qf[kk], kk == 0 ? zero16 : s[kb]);
-                }
+            for (int kk = 1; kk < D / 16; ++kk) {
+                const u32x4_t kop = *reinterpret_cast<const u32x4_t *>(ks + k_rd[kk] + 32 * kb * D);
+                s[kb] = mfma_32x32x16_bf16(kop, qf[kk], s[kb]);
             }
+        }
+        if constexpr (masked) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = kv0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
+                    const bool vis = key < a.Sk && (!CAUSAL || key <= my_q + diag);
+                    s[kb][v] = vis ? s[kb][v] : kNegInf;
+                }
         }
         // Row max of the raw scores (c >= 0, so scaling preserves order).
         float mraw = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                if constexpr (MASKED) {
-                    const int key = kv0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
-                    const bool vis = key < a.Sk && (!CAUSAL || key <= my_q + diag);
-                    s[kb][v] = vis ? s[kb][v] : kNegInf;
-                }
-                mraw = fmaxf(mraw, s[kb][v]);
-            }
+            for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, s[kb][v]);
         mraw = pair_max_halves(mraw);
         const float mx = mraw == kNegInf ? kNegInf : mraw * c;
         const float m_new = fmaxf(m, mx);
         const bool grow = m_new > m + 8.0f;
         if (wave_any(grow)) {
+            keep_branch();
             const float alpha = grow ? exp2_fast(m - m_new) : 1.0f;
             m = grow ? m_new : m;
             lsum *= alpha;
@@ -246,7 +254,19 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
             for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
         }
         const float nm = (m == kNegInf) ? 0.f : -m;
-        // P = 2^(s c - m) -> bf16 pairs; the row sum adds the rounded values.
+        // Exponents s c - m; masked scores stay -inf (also when c == 0).
+        float x[2][16];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) x[kb][v] = __builtin_fmaf(s[kb][v], c, nm);
+        if constexpr (masked) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) x[kb][v] = s[kb][v] == kNegInf ? kNegInf : x[kb][v];
+        }
+        // P = 2^x -> bf16 pairs; the row sum adds the fp32 values.
         u32x4_t pk[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -254,20 +274,13 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
             for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float x0 = __builtin_fmaf(s[kb][8 * cc + 2 * e], c, nm);
-                    float x1 = __builtin_fmaf(s[kb][8 * cc + 2 * e + 1], c, nm);
-                    if constexpr (MASKED) {
-                        x0 = s[kb][8 * cc + 2 * e] == kNegInf ? kNegInf : x0;
-                        x1 = s[kb][8 * cc + 2 * e + 1] == kNegInf ? kNegInf : x1;
-                    }
-                    const float p0 = exp2_fast(x0), p1 = exp2_fast(x1);
+                    const float p0 = exp2_fast(x[kb][8 * cc + 2 * e]), p1 = exp2_fast(x[kb][8 * cc + 2 * e + 1]);
                     pk[kb][cc][e] = pack_bf16x2(p0, p1);
                     lsum += p0 + p1;
                 }
-        // O^T += V^T P^T over the live halves.
+        // O^T += V^T P^T
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            if (!live[kb]) continue;
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 const int kbase_el = (32 * kb + 16 * cc) * D;
@@ -282,23 +295,26 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
         }
     };
 
-    // Tiles before `first_masked` are fully visible to every row of this wave.
-    int first_masked = a.Sk / kBC;                       // full tiles inside the sequence
-    if (CAUSAL) first_masked = min(first_masked, max(0, (q0 + diag + 1) / kBC));
-    auto run_tile = [&](const uint16_t *ks, const uint16_t *vs, int j) __attribute__((always_inline)) {
-        if (j >= first_masked) compute_tile(ks, vs, j, std::true_type{});
-        else compute_tile(ks, vs, j, std::false_type{});
-    };
-
+    // Tiles [0, fm) need no mask for this wave: they run in a branch-free
+    // loop over the two static stages.  The remaining tiles (those crossing
+    // the diagonal or the end of the keys, and an odd leftover) run through
+    // the masked body.  Every wave passes one barrier per tile either way.
+    const int fm = min(first_masked, ntiles);
     if (ntiles > 0) issue_tile(0, k_st0, v_st0);
     __syncthreads();
-    for (int j = 0; j < ntiles; j += 2) {
-        if (j + 1 < ntiles) issue_tile(j + 1, k_st1, v_st1);
-        run_tile(k_st0, v_st0, j);
+    int j = 0;
+    for (; j + 1 < fm; j += 2) {
+        issue_tile(j + 1, k_st1, v_st1);
+        run_tile(k_st0, v_st0, j, std::false_type{});
         __syncthreads();
-        if (j + 1 >= ntiles) break;
         if (j + 2 < ntiles) issue_tile(j + 2, k_st0, v_st0);
-        run_tile(k_st1, v_st1, j + 1);
+        run_tile(k_st1, v_st1, j + 1, std::false_type{});
+        __syncthreads();
+    }
+    for (; j < ntiles; ++j) {
+        uint16_t *ks = (j & 1) ? k_st1 : k_st0, *vs = (j & 1) ? v_st1 : v_st0;
+        if (j + 1 < ntiles) issue_tile(j + 1, (j & 1) ? k_st0 : k_st1, (j & 1) ? v_st0 : v_st1);
+        run_tile(ks, vs, j, std::true_type{});
         __syncthreads();
     }
 
