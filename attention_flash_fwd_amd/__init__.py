@@ -98,6 +98,40 @@ def decode_workspace(q, k_cache, block_table, num_splits=0):
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
 
 
+def prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, causal: bool = True,
+                  scale: float | None = None, out=None, lse_out=None, return_lse: bool = True):
+    """A chunk of Sq new query tokens per sequence over a paged bf16 KV cache
+    that already holds the chunk's own keys (chunked prefill).
+
+    q [B,Sq,Hq,D]; k_cache/v_cache [num_blocks,16,Hkv,D]; block_table
+    [B,max_blocks] int32; ctx_lens [B] int32 (keys per sequence, chunk
+    included).  Returns (o [B,Sq,Hq,D] bf16, lse [B,Hq,Sq] fp32 or None)."""
+    import torch
+    lib = _lib.load()
+    _need_gpu(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out)
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise TypeError("prefill_paged takes bf16 q and caches")
+    if block_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
+        raise TypeError("block_table and ctx_lens must be int32")
+    B, Sq, Hq, D = q.shape
+    nblocks, bs, Hkv, Dk = k_cache.shape
+    if Dk != D or v_cache.shape != k_cache.shape or block_table.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("inconsistent prefill_paged shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = out if out is not None else torch.empty_like(q)
+    lse = lse_out
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    st = lib.attn_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                _ptr(ctx_lens), _ptr(o), _ptr(lse),
+                                B, Sq, Hq, Hkv, D, nblocks, bs, block_table.shape[1],
+                                1 if causal else 0, float(scale), _stream_handle(q))
+    if st != _lib.ATTN_OK:
+        raise AttnError(st, "attn_prefill_paged")
+    return o, lse
+
+
 def decode_paged(q, k_cache, v_cache, block_table, ctx_lens, num_splits: int = 0,
                  scale: float | None = None, out=None, lse_out=None, workspace=None,
                  return_lse: bool = True):

@@ -23,7 +23,7 @@ ATTN_F32 = 1
 MAX_SPLITS = 256
 
 # Every symbol include/attn.h declares.
-EXPORTED = ("attn_prefill", "attn_decode_paged", "attn_decode_workspace_bytes",
+EXPORTED = ("attn_prefill", "attn_prefill_paged", "attn_decode_paged", "attn_decode_workspace_bytes",
             "attn_decode_num_splits", "attn_status_string", "attn_abi_version")
 
 _lib = None
@@ -42,6 +42,8 @@ def _declare(lib):
     Z = ctypes.c_size_t
     lib.attn_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
     lib.attn_prefill.restype = I
+    lib.attn_prefill_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P]
+    lib.attn_prefill_paged.restype = I
     lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, Z, P]
     lib.attn_decode_paged.restype = I
     lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, I]

@@ -90,7 +90,7 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
                                      n_kv_heads, head_dim, dtype);
     if (st != ATTN_OK || batch == 0 || seqlen_q == 0) return st;
 
-    attn::PrefillArgs a;
+    attn::PrefillArgs a = {};
     a.q = q;
     a.k = k;
     a.v = v;
@@ -105,6 +105,52 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v, void *o,
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = dtype == ATTN_BF16 ? attn::launch_prefill_bf16(a, head_dim, causal != 0, s)
                                       : attn::launch_prefill_f32(a, head_dim, causal != 0, s);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status_t attn_prefill_paged(const void *q, const void *k_cache, const void *v_cache,
+                                 const int32_t *block_table, const int32_t *ctx_lens,
+                                 void *o, float *lse,
+                                 int batch, int seqlen_q, int n_q_heads, int n_kv_heads, int head_dim,
+                                 int num_blocks, int block_size, int max_blocks_per_seq,
+                                 int causal, float scale, attn_stream_t stream)
+{
+    if (batch < 0 || seqlen_q < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 ||
+        num_blocks < 0 || max_blocks_per_seq < 0 || block_size <= 0)
+        return ATTN_ERR_SHAPE;
+    if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+    if (block_size != kBlockSize) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)batch * seqlen_q * n_q_heads * head_dim >= kMaxElems) return ATTN_ERR_SHAPE;
+    if ((long long)max_blocks_per_seq * block_size >= kMaxElems) return ATTN_ERR_SHAPE;
+    // One cache block of one KV head must stay addressable by 32-bit offsets.
+    if ((long long)block_size * n_kv_heads * head_dim * 2 >= (1LL << 31)) return ATTN_ERR_SHAPE;
+    if (batch == 0 || seqlen_q == 0) return ATTN_OK;
+    if (q == nullptr || o == nullptr || block_table == nullptr || ctx_lens == nullptr)
+        return ATTN_ERR_NULL;
+    if (num_blocks > 0 && (k_cache == nullptr || v_cache == nullptr)) return ATTN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+        return ATTN_ERR_ALIGN;
+    if (!aligned(block_table, 4) || !aligned(ctx_lens, 4)) return ATTN_ERR_ALIGN;
+    if (lse != nullptr && !aligned(lse, 4)) return ATTN_ERR_ALIGN;
+
+    attn::PrefillArgs a = {};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.o = o;
+    a.lse = lse;
+    a.B = batch;
+    a.Sq = seqlen_q;
+    a.Sk = 0;
+    a.Hq = n_q_heads;
+    a.Hkv = n_kv_heads;
+    a.scale_log2 = scale * kLog2e;
+    a.block_table = block_table;
+    a.ctx_lens = ctx_lens;
+    a.num_blocks = num_blocks;
+    a.max_blocks = max_blocks_per_seq;
+    hipError_t e = attn::launch_prefill_paged_bf16(a, head_dim, causal != 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -9,10 +9,15 @@ namespace attn {
 
 struct PrefillArgs {
     const void *q, *k, *v;    // [B,Sq,Hq,D], [B,Sk,Hkv,D], [B,Sk,Hkv,D]
+                              // (paged: k, v are caches [num_blocks,16,Hkv,D])
     void *o;                  // [B,Sq,Hq,D]
     float *lse;               // [B,Hq,Sq] or nullptr
-    int B, Sq, Sk, Hq, Hkv;
+    int B, Sq, Sk, Hq, Hkv;   // paged: Sk unused, keys per sequence in ctx_lens
     float scale_log2;         // softmax scale times log2(e)
+    // Paged keys and values only:
+    const int32_t *block_table;   // [B,max_blocks]
+    const int32_t *ctx_lens;      // [B]
+    int num_blocks, max_blocks;
 };
 
 struct DecodeArgs {
@@ -31,6 +36,7 @@ struct DecodeArgs {
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, int head_dim, bool causal, hipStream_t s);
+hipError_t launch_prefill_paged_bf16(const PrefillArgs &a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int head_dim, hipStream_t s);
 
 }  // namespace attn

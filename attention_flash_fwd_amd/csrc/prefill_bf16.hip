@@ -49,6 +49,7 @@ namespace {
 
 constexpr int kBR = 128;      // query rows per workgroup
 constexpr int kBC = 64;       // keys per K/V tile
+constexpr int kBS = 16;       // tokens per cache block (paged keys and values)
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 
@@ -96,7 +97,7 @@ __device__ __forceinline__ void map_workgroup(int L, const PrefillArgs &a, int n
     qt = n_qtiles - 1 - qt_rev;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PAGED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
 {
@@ -116,10 +117,22 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
     const int i0 = qt * kBR;
     const int q0 = i0 + wave * 32;      // first query row of this wave (uniform)
     const int my_q = q0 + l32;          // query row of this lane
-    const int diag = a.Sk - a.Sq;       // key j visible to row i iff j <= i + diag
+    // Keys of this sequence.  Paged: read through the scalar cache (so that
+    // everything derived from it stays wave-uniform); a length outside the
+    // table's reach marks the sequence bad (NaN output) and reads no key.
+    int Sk = a.Sk;
+    bool bad = false;
+    if constexpr (PAGED) {
+        Sk = ((const int32_t __attribute__((address_space(4))) *)a.ctx_lens)[b];
+        if (Sk < 0 || Sk > a.max_blocks * kBS) {
+            bad = true;
+            Sk = 0;
+        }
+    }
+    const int diag = Sk - a.Sq;         // key j visible to row i iff j <= i + diag
 
-    int kend = a.Sk;                    // keys [0, kend) may be visible to this workgroup
-    if (CAUSAL) kend = min(a.Sk, min(a.Sq, i0 + kBR) + diag);
+    int kend = Sk;                      // keys [0, kend) may be visible to this workgroup
+    if (CAUSAL) kend = min(Sk, min(a.Sq, i0 + kBR) + diag);
     const int ntiles = kend > 0 ? (kend + kBC - 1) / kBC : 0;
 
     // Exponent scale c = scale * log2(e), made non-negative by flipping the
@@ -144,11 +157,11 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
 
     // ---- K/V streaming: buffer loads that write LDS directly ------------
     const uint32_t row_bytes = (uint32_t)(a.Hkv * D * 2);
-    const size_t head_off = ((size_t)b * a.Sk * a.Hkv + hk) * D;      // elements
+    const size_t head_off = PAGED ? 0 : ((size_t)b * a.Sk * a.Hkv + hk) * D;      // elements
     const char *kbase = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k) + head_off);
     const char *vbase = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.v) + head_off);
     // Bytes from this head's first key to the end of its last key row.
-    const uint32_t span = a.Sk > 0 ? (uint32_t)(((size_t)(a.Sk - 1) * a.Hkv * D + D) * 2) : 0u;
+    const uint32_t span = Sk > 0 ? (uint32_t)(((size_t)(Sk - 1) * a.Hkv * D + D) * 2) : 0u;
 
     // Per-lane source offsets (bytes, relative to the tile's first key) of the
     // 16-byte chunks this lane's LDS-direct loads deliver: load i of wave w
@@ -159,14 +172,47 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
         const int slot = (wave * T::loads_per_wave + i) * 64 + lane;
         const int r = slot / T::cpr, p = slot % T::cpr;
         const int cl = T::swz(r, p);                      // swz is an involution
-        src_off[i] = (uint32_t)r * row_bytes + (uint32_t)cl * 16u;
+        // Paged: the wave's 16 rows are one cache block; offsets are relative
+        // to this head's slice of that block's first token.
+        src_off[i] = (uint32_t)(PAGED ? r - kBS * wave : r) * row_bytes + (uint32_t)cl * 16u;
     }
 
+    // Paged: wave w loads cache block 4 j + w of tile j (its 16 rows).  The
+    // physical block ids come through the scalar cache one tile ahead.
+    const int n_lblocks = (Sk + kBS - 1) / kBS;
+    const int32_t __attribute__((address_space(4))) *tb =
+        (const int32_t __attribute__((address_space(4))) *)(a.block_table + (PAGED ? (size_t)b * a.max_blocks : 0));
+    int phys_next = (PAGED && wave < n_lblocks) ? tb[wave] : 0;
+    const uint32_t blk_bytes = (uint32_t)kBS * row_bytes;
+
     auto issue_tile = [&](int j, uint16_t *ks, uint16_t *vs) __attribute__((always_inline)) {
-        const uint32_t start = (uint32_t)(j * kBC) * row_bytes;
-        const uint32_t left = span > start ? span - start : 0u;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + start, left);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + start, left);
+        __amdgpu_buffer_rsrc_t rk, rv;
+        if constexpr (PAGED) {
+            const int lb = (kBC / kBS) * j + wave;
+            const int p = phys_next;
+            phys_next = lb + kBC / kBS < n_lblocks ? tb[lb + kBC / kBS] : 0;
+            int valid = min(kBS, Sk - kBS * lb);
+            long long phys = 0;
+            if (valid > 0) {
+                if (p < 0 || p >= a.num_blocks) {
+                    bad = true;
+                    valid = 0;
+                } else {
+                    phys = p;
+                }
+            } else {
+                valid = 0;
+            }
+            const size_t off = (size_t)phys * blk_bytes + (size_t)hk * D * 2;
+            const uint32_t num = valid > 0 ? (uint32_t)(valid - 1) * row_bytes + D * 2 : 0u;
+            rk = make_rsrc(static_cast<const char *>(a.k) + off, num);
+            rv = make_rsrc(static_cast<const char *>(a.v) + off, num);
+        } else {
+            const uint32_t start = (uint32_t)(j * kBC) * row_bytes;
+            const uint32_t left = span > start ? span - start : 0u;
+            rk = make_rsrc(kbase + start, left);
+            rv = make_rsrc(vbase + start, left);
+        }
 #pragma unroll
         for (int i = 0; i < T::loads_per_wave; ++i) {
             const int chunk0 = (wave * T::loads_per_wave + i) * 64;      // uniform
@@ -204,7 +250,7 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
     const f32x16_t zero16 = {};
 
     // Tiles before `first_masked` are fully visible to every row of this wave.
-    int first_masked = a.Sk / kBC;                       // full tiles inside the sequence
+    int first_masked = Sk / kBC;                         // full tiles inside the sequence
     if (CAUSAL) first_masked = min(first_masked, max(0, (q0 + diag + 1) / kBC));
 
     // One code path for every tile: masking is a uniform branch around the
@@ -231,7 +277,7 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int key = kv0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
-                    const bool vis = key < a.Sk && (!CAUSAL || key <= my_q + diag);
+                    const bool vis = key < Sk && (!CAUSAL || key <= my_q + diag);
                     s[kb][v] = vis ? s[kb][v] : kNegInf;
                 }
         }
@@ -319,9 +365,11 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
     }
 
     // ---- epilogue ----------------------------------------------------------
+    if constexpr (PAGED) bad = __syncthreads_or(bad);
     const float ltot = pair_sum_halves(lsum);
     if (my_q < a.Sq) {
-        const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+        float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+        if (PAGED && bad) inv = __builtin_nanf("");
         uint16_t *op = static_cast<uint16_t *>(a.o) + (((size_t)b * a.Sq + my_q) * a.Hq + hq) * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
@@ -334,17 +382,18 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
             }
         }
         if (a.lse != nullptr && h == 0)
-            a.lse[((size_t)b * a.Hq + hq) * a.Sq + my_q] = ltot > 0.f ? (m + __log2f(ltot)) * kLn2 : kNegInf;
+            a.lse[((size_t)b * a.Hq + hq) * a.Sq + my_q] =
+                (PAGED && bad) ? __builtin_nanf("") : (ltot > 0.f ? (m + __log2f(ltot)) * kLn2 : kNegInf);
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PAGED>
 hipError_t launch_one(const PrefillArgs &a, hipStream_t s)
 {
     const int n_qtiles = (a.Sq + kBR - 1) / kBR;
     const long long grid = (long long)n_qtiles * a.Hq * a.B;
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, n_qtiles);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, PAGED>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, n_qtiles);
     return hipGetLastError();
 }
 
@@ -352,8 +401,15 @@ hipError_t launch_one(const PrefillArgs &a, hipStream_t s)
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, bool causal, hipStream_t s)
 {
-    if (head_dim == 128) return causal ? launch_one<128, true>(a, s) : launch_one<128, false>(a, s);
-    if (head_dim == 64) return causal ? launch_one<64, true>(a, s) : launch_one<64, false>(a, s);
+    if (head_dim == 128) return causal ? launch_one<128, true, false>(a, s) : launch_one<128, false, false>(a, s);
+    if (head_dim == 64) return causal ? launch_one<64, true, false>(a, s) : launch_one<64, false, false>(a, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_paged_bf16(const PrefillArgs &a, int head_dim, bool causal, hipStream_t s)
+{
+    if (head_dim == 128) return causal ? launch_one<128, true, true>(a, s) : launch_one<128, false, true>(a, s);
+    if (head_dim == 64) return causal ? launch_one<64, true, true>(a, s) : launch_one<64, false, true>(a, s);
     return hipErrorInvalidValue;
 }
 

@@ -100,7 +100,37 @@ DECODE_B64 = DecodeConfig("paged_decode_b64_h32kv8_d128_ctx512-32768_bf16", 64, 
 DECODE_128K = DecodeConfig("paged_decode_b4_h64kv8_d128_ctx131072_bf16", 4, 64, 8, 128,
                            131072, 131072, 64, 5)
 
-CONFIGS = {c.name: c for c in (TINY_F32, PREFILL_2K, PREFILL_8K, DECODE_B64, DECODE_128K)}
+
+
+@dataclass(frozen=True)
+class ChunkedPrefillConfig:
+    """The last ``chunk`` tokens of ``batch`` prompts of ``ctx`` tokens whose
+    keys and values sit in a shuffled paged cache (chunked prefill)."""
+    name: str
+    batch: int
+    ctx: int
+    chunk: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    def flops(self) -> float:
+        """Algorithmic FLOPs over the visible (query, key) pairs: query i of
+        the chunk sees ctx - chunk + i + 1 keys."""
+        pairs = self.chunk * (self.ctx - self.chunk) + self.chunk * (self.chunk + 1) // 2
+        return 4.0 * self.head_dim * self.batch * self.n_q_heads * pairs
+
+
+CHUNKED_PREFILL = ChunkedPrefillConfig("chunked_prefill_b2_ctx8192_chunk2048_h32kv8_d128_bf16",
+                                       2, 8192, 2048, 32, 8, 128, 6)
+
+CONFIGS = {c.name: c for c in (TINY_F32, PREFILL_2K, PREFILL_8K, DECODE_B64, DECODE_128K,
+                               CHUNKED_PREFILL)}
 
 
 # --------------------------------------------------------------------------
@@ -211,6 +241,13 @@ def decode_inputs(ctx, n_q_heads, n_kv_heads, head_dim, seed=0, device="cpu",
                        ctx_lens=torch.tensor(ctx, dtype=torch.int32, device=dev),
                        seed=int(seed), device=str(dev), block_size=block_size, ctx=ctx)
     return inp
+
+
+def chunk_queries(batch, seqlen_q, n_q_heads, head_dim, seed=0, device="cpu"):
+    """Queries of a prefill chunk, [B, Sq, Hq, D] bf16: the last Sq tokens of
+    each sequence whose keys and values ``decode_inputs`` placed in the cache
+    (drawn from their own seed stream, independent of the cache values)."""
+    return _normal((batch, seqlen_q, n_q_heads, head_dim), seed, "q", 1, device, torch.bfloat16)
 
 
 def decode_config_inputs(cfg: DecodeConfig, device="cpu"):

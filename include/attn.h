@@ -1,7 +1,7 @@
 /*
  * attn.h -- exact attention forward on AMD Instinct MI355X (gfx950).
  *
- * C ABI of libattn.so.  Two operations:
+ * C ABI of libattn.so.  Three operations:
  *
  *   attn_prefill       exact scaled-dot-product attention over whole
  *                      sequences (optionally causal, grouped-query heads),
@@ -16,6 +16,10 @@
  *                      standard attention; chenyy20.com "抱infra脚", section
  *                      Flash Attention 基本原理 / 核心技术: tiling, online
  *                      softmax and kernel fusion of QK + softmax + PV.)
+ *
+ *   attn_prefill_paged the same over a paged KV cache, for a chunk of new
+ *                      query tokens at the end of each cached sequence
+ *                      (chunked prefill).
  *
  *   attn_decode_paged  one new query token per sequence against a paged KV
  *                      cache, Flash-Decoding style: the cached keys of each
@@ -112,6 +116,43 @@ attn_status_t attn_prefill(const void *q, const void *k, const void *v,
                            attn_stream_t stream);
 
 /*
+ * attn_prefill_paged -- exact attention of a chunk of new query tokens over
+ * keys and values held in a paged cache: the prefill of one chunk of a long
+ * prompt whose earlier chunks (and this chunk's own keys and values) are
+ * already cached.  ("抱infra脚", sections Chunked Prefill and Paged
+ * Attention: a long prompt is processed a chunk at a time against the cache,
+ * whose fixed-size blocks are reached through a block table; "推理加速"
+ * interview notes, section FlashAttention, for the computation itself.)
+ *
+ *   q            [batch, seqlen_q, n_q_heads, head_dim]             bf16
+ *   k_cache      [num_blocks, block_size, n_kv_heads, head_dim]     bf16
+ *   v_cache      [num_blocks, block_size, n_kv_heads, head_dim]     bf16
+ *   block_table  [batch, max_blocks_per_seq] int32 (as attn_decode_paged)
+ *   ctx_lens     [batch] int32: cached keys of each sequence, including the
+ *                seqlen_q keys of this chunk, which are its last ones
+ *   o            [batch, seqlen_q, n_q_heads, head_dim] bf16, written
+ *   lse          [batch, n_q_heads, seqlen_q] fp32, written; may be NULL
+ *
+ * Query i of sequence b is the token at position ctx_lens[b] - seqlen_q + i,
+ * so with causal != 0 it sees keys j <= i + ctx_lens[b] - seqlen_q (the
+ * bottom-right alignment of attn_prefill with seqlen_k = ctx_lens[b]); a row
+ * with no visible key gets O = 0, lse = -inf.  Without causal every cached
+ * key is visible.  Cache slots past ctx_lens[b] are never read.
+ *
+ * Supported: bf16, head_dim 64 or 128, block_size 16.  Device-side contract
+ * violations do not fault: a sequence whose ctx_lens entry is negative or
+ * exceeds max_blocks_per_seq * block_size, or whose needed block ids fall
+ * outside [0, num_blocks), gets NaN in o and lse.  Host-side checks and
+ * status codes are those of attn_decode_paged (no workspace).
+ */
+attn_status_t attn_prefill_paged(const void *q, const void *k_cache, const void *v_cache,
+                                 const int32_t *block_table, const int32_t *ctx_lens,
+                                 void *o, float *lse,
+                                 int batch, int seqlen_q, int n_q_heads, int n_kv_heads, int head_dim,
+                                 int num_blocks, int block_size, int max_blocks_per_seq,
+                                 int causal, float scale, attn_stream_t stream);
+
+/*
  * attn_decode_num_splits -- the number of key chunks per sequence that
  * attn_decode_paged will use for these arguments.  num_splits >= 1 is
  * returned unchanged (after the range check of attn_decode_paged);
@@ -180,7 +221,7 @@ const char *attn_status_string(attn_status_t status);
 /* ABI version of this header: (major << 16) | minor. */
 int attn_abi_version(void);
 
-#define ATTN_ABI_VERSION ((1 << 16) | 0)
+#define ATTN_ABI_VERSION ((1 << 16) | 1)
 
 #ifdef __cplusplus
 }

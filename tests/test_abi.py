@@ -37,7 +37,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     fns = header_functions()
-    for name in ("attn_prefill", "attn_decode_paged", "attn_decode_workspace_bytes",
+    for name in ("attn_prefill", "attn_prefill_paged", "attn_decode_paged", "attn_decode_workspace_bytes",
                  "attn_decode_num_splits", "attn_status_string", "attn_abi_version"):
         assert name in fns
     assert set(fns) == set(_lib.EXPORTED)
@@ -59,7 +59,7 @@ def test_exports_are_c_symbols():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.attn_abi_version() == (1 << 16)
+    assert lib.attn_abi_version() == (1 << 16) | 1
     for code in range(8):
         s = lib.attn_status_string(code).decode()
         assert s and s != "unknown status"
@@ -125,6 +125,34 @@ def test_decode_validation(lib):
     need = lib.attn_decode_workspace_bytes(2, 8, 2, 128, 5, 16, 4)
     assert decode(lib, ws_bytes=need - 1) == WORKSPACE
     assert decode(lib, B=0, q=0, o=0, tbl=0, ctx=0) == OK
+
+
+def prefill_paged(lib, q=FAKE, kc=FAKE, vc=FAKE, tbl=FAKE, ctx=FAKE, o=FAKE, lse=FAKE, B=2, Sq=8,
+                  Hq=8, Hkv=2, D=128, nblocks=10, bs=16, max_blocks=5, causal=1, scale=0.1):
+    P = ctypes.c_void_p
+    return lib.attn_prefill_paged(P(q), P(kc), P(vc), P(tbl), P(ctx), P(o), P(lse), B, Sq, Hq, Hkv, D,
+                                  nblocks, bs, max_blocks, causal, scale, P(0))
+
+
+def test_prefill_paged_validation(lib):
+    assert prefill_paged(lib, D=96) == UNSUP
+    assert prefill_paged(lib, bs=32) == UNSUP
+    assert prefill_paged(lib, Hq=6, Hkv=4) == SHAPE
+    assert prefill_paged(lib, B=-1) == SHAPE
+    assert prefill_paged(lib, Sq=-1) == SHAPE
+    assert prefill_paged(lib, nblocks=-1) == SHAPE
+    assert prefill_paged(lib, Hkv=1 << 20, Hq=1 << 20) == SHAPE     # a block past 2^31 bytes
+    assert prefill_paged(lib, q=0) == NULL
+    assert prefill_paged(lib, tbl=0) == NULL
+    assert prefill_paged(lib, ctx=0) == NULL
+    assert prefill_paged(lib, vc=0) == NULL
+    assert prefill_paged(lib, o=0) == NULL
+    assert prefill_paged(lib, q=FAKE_MIS) == ALIGN
+    assert prefill_paged(lib, vc=FAKE_MIS) == ALIGN
+    assert prefill_paged(lib, ctx=FAKE + 2) == ALIGN
+    assert prefill_paged(lib, lse=FAKE + 2) == ALIGN
+    assert prefill_paged(lib, B=0, q=0, o=0, tbl=0, ctx=0) == OK
+    assert prefill_paged(lib, Sq=0, q=0, o=0, tbl=0, ctx=0) == OK
 
 
 def test_workspace_and_split_rules(lib):

@@ -319,3 +319,111 @@ def test_decode_full_size_sampled(afa, cfg_name, nseq):
     check_lse(to_np(lse)[seqs], l_ref, BF16_LSE_ABS)
     del inp
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------ paged (chunked) prefill ---
+def gen_paged_prefill(ctx, Sq, Hq, Hkv, D, seed, **kw):
+    from attention_flash_fwd_amd import inputs
+    inp = inputs.decode_inputs(ctx, Hq, Hkv, D, seed=seed, device="cuda", **kw)
+    q = inputs.chunk_queries(len(ctx), Sq, Hq, D, seed=seed, device="cuda")
+    return inp, q
+
+
+def paged_prefill_oracle(inp, q, causal, scale, seqs=None):
+    qn = to_np(q)
+    os_, ls_ = [], []
+    for b in (range(len(inp.ctx)) if seqs is None else seqs):
+        kb, vb = inp.logical_kv(b, device="cpu")
+        o, l = oracle.attention(qn[b:b + 1], kb.float().numpy()[None], vb.float().numpy()[None],
+                                causal, scale)
+        os_.append(o[0])
+        ls_.append(l[0])
+    return np.stack(os_), np.stack(ls_)
+
+
+@pytest.mark.parametrize("ctx,Sq,Hq,Hkv,D,causal", [
+    ([300, 77, 1000, 130], 70, 8, 2, 128, True),     # ragged lengths, GQA
+    ([16, 200], 70, 8, 2, 128, True),                # ctx < Sq: leading rows see no key
+    ([513, 64], 64, 4, 4, 128, False),               # non-causal, MHA
+    ([129, 700], 130, 32, 8, 128, True),             # several q-tiles and a ragged tail
+    ([390, 45], 45, 8, 1, 64, True),                 # D = 64, G = 8, Sq = ctx for one sequence
+])
+def test_prefill_paged_small(afa, ctx, Sq, Hq, Hkv, D, causal):
+    say(f"case prefill_paged ctx{ctx} Sq{Sq} Hq{Hq} Hkv{Hkv} D{D} causal{causal}")
+    inp, q = gen_paged_prefill(ctx, Sq, Hq, Hkv, D, seed=sum(ctx) + Sq, spare_blocks=3)
+    scale = 1 / math.sqrt(D)
+    o, lse = afa.prefill_paged(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                               causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = paged_prefill_oracle(inp, q, causal, scale)
+    check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse), l_ref, BF16_LSE_ABS)
+
+
+def test_prefill_paged_equals_contiguous_and_permutation(afa):
+    # With the whole sequence as the chunk, paged prefill is the contiguous
+    # prefill on the same keys: same kernel arithmetic, bit-identical output.
+    say("case prefill_paged == prefill / block permutation")
+    S, Hq, Hkv, D = 333, 16, 4, 128
+    inp, q = gen_paged_prefill([S, S], S, Hq, Hkv, D, seed=21, spare_blocks=5)
+    k = torch.stack([inp.logical_kv(b)[0] for b in range(2)]).contiguous()
+    v = torch.stack([inp.logical_kv(b)[1] for b in range(2)]).contiguous()
+    o_c, l_c = afa.prefill(q, k, v, causal=True)
+    o_p, l_p = afa.prefill_paged(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens)
+    torch.cuda.synchronize()
+    assert torch.equal(o_c, o_p) and torch.equal(l_c, l_p)
+    nb = inp.k_cache.shape[0]
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(2)).cuda()
+    k2 = torch.empty_like(inp.k_cache)
+    v2 = torch.empty_like(inp.v_cache)
+    k2[perm] = inp.k_cache
+    v2[perm] = inp.v_cache
+    tbl = inp.block_table.long()
+    tbl2 = torch.where(tbl >= 0, perm[tbl.clamp(min=0)], tbl).to(torch.int32).contiguous()
+    o_q, l_q = afa.prefill_paged(q, k2, v2, tbl2, inp.ctx_lens)
+    torch.cuda.synchronize()
+    assert torch.equal(o_p, o_q) and torch.equal(l_p, l_q)
+
+
+def test_prefill_paged_zero_context_and_contract_violations(afa):
+    say("case prefill_paged ctx 0 / bad block ids / oversize ctx")
+    inp, q = gen_paged_prefill([0, 50, 50, 50], 20, 8, 2, 128, seed=9)
+    tbl = inp.block_table.clone()
+    tbl[2, 1] = inp.k_cache.shape[0] + 3           # block id past the pool
+    ctx = inp.ctx_lens.clone()
+    ctx[3] = inp.block_table.shape[1] * 16 + 1     # more tokens than the table can hold
+    o, lse = afa.prefill_paged(q, inp.k_cache, inp.v_cache, tbl, ctx)
+    torch.cuda.synchronize()
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.isfinite(o[1]).all() and torch.isfinite(lse[1]).all()
+    assert torch.isnan(o[2]).all() and torch.isnan(lse[2]).all()
+    assert torch.isnan(o[3]).all() and torch.isnan(lse[3]).all()
+    o_ref, l_ref = paged_prefill_oracle(inp, q, True, 1 / math.sqrt(128), seqs=[1])
+    check_o(to_np(o[1:2]), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse[1:2]), l_ref, BF16_LSE_ABS)
+
+
+def test_prefill_paged_long_chunk_sampled(afa):
+    # The last 2048-token chunk of two 8192-token prompts (the benchmark's
+    # chunked-prefill workload), compared on sampled query rows.
+    from attention_flash_fwd_amd import inputs
+    cfg = inputs.CHUNKED_PREFILL
+    say(f"case {cfg.name} (sampled rows)")
+    inp, q = gen_paged_prefill([cfg.ctx] * cfg.batch, cfg.chunk, cfg.n_q_heads, cfg.n_kv_heads,
+                               cfg.head_dim, seed=cfg.seed)
+    o, lse = afa.prefill_paged(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                               causal=True, scale=cfg.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(5)
+    qn = to_np(q)
+    rows = [(int(rng.integers(cfg.batch)), int(rng.integers(cfg.n_q_heads)), int(rng.integers(cfg.chunk)))
+            for _ in range(48)] + [(0, 0, 0), (cfg.batch - 1, cfg.n_q_heads - 1, cfg.chunk - 1)]
+    kv = [inp.logical_kv(b, device="cpu") for b in range(cfg.batch)]
+    k = np.stack([x[0].float().numpy() for x in kv])
+    v = np.stack([x[1].float().numpy() for x in kv])
+    o_ref, l_ref = oracle.attention_rows(qn, k, v, True, cfg.scale, rows)
+    got = np.stack([to_np(o[b, i, h]) for (b, h, i) in rows])
+    got_l = np.array([lse[b, h, i].item() for (b, h, i) in rows])
+    check_o(got, o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(got_l, l_ref, BF16_LSE_ABS)
