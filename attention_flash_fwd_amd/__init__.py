@@ -90,11 +90,17 @@ def decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, max_blocks_pe
 
 
 def decode_workspace(q, k_cache, block_table, num_splits=0):
-    """Allocate a workspace tensor sized for these decode arguments."""
+    """Allocate a workspace tensor sized for these decode arguments (q is
+    [B,Hq,D] for decode_paged or [B,T,Hq,D] for decode_paged_multi)."""
     import torch
-    B, Hq, D = q.shape
-    nbytes = decode_workspace_bytes(B, Hq, k_cache.shape[2], D, block_table.shape[1],
-                                    k_cache.shape[1], num_splits)
+    if q.dim() == 3:
+        B, Hq, D = q.shape
+        T = 1
+    else:
+        B, T, Hq, D = q.shape
+    nbytes = int(_lib.load().attn_decode_multi_workspace_bytes(B, T, Hq, k_cache.shape[2], D,
+                                                               block_table.shape[1], k_cache.shape[1],
+                                                               num_splits))
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
 
 
@@ -129,6 +135,41 @@ def prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, causal: bool = Tru
                                 1 if causal else 0, float(scale), _stream_handle(q))
     if st != _lib.ATTN_OK:
         raise AttnError(st, "attn_prefill_paged")
+    return o, lse
+
+
+def decode_paged_multi(q, k_cache, v_cache, block_table, ctx_lens, num_splits: int = 0,
+                       scale: float | None = None, out=None, lse_out=None, workspace=None,
+                       return_lse: bool = True):
+    """T new query tokens per sequence (causal among themselves) over a paged
+    bf16 KV cache that already holds their keys, as in speculative-decoding
+    verification.  q [B,T,Hq,D]; other arguments as for decode_paged.
+    Returns (o [B,T,Hq,D] bf16, lse [B,Hq,T] fp32 or None)."""
+    import torch
+    lib = _lib.load()
+    _need_gpu(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out, workspace)
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise TypeError("decode_paged_multi takes bf16 q and caches")
+    if block_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
+        raise TypeError("block_table and ctx_lens must be int32")
+    B, T, Hq, D = q.shape
+    nblocks, bs, Hkv, Dk = k_cache.shape
+    if Dk != D or v_cache.shape != k_cache.shape or block_table.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("inconsistent decode shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = decode_workspace(q, k_cache, block_table, num_splits)
+    o = out if out is not None else torch.empty_like(q)
+    lse = lse_out
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    st = lib.attn_decode_paged_multi(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                     _ptr(ctx_lens), _ptr(o), _ptr(lse), B, T, Hq, Hkv, D, nblocks, bs,
+                                     block_table.shape[1], int(num_splits), float(scale),
+                                     _ptr(workspace), workspace.numel(), _stream_handle(q))
+    if st != _lib.ATTN_OK:
+        raise AttnError(st, "attn_decode_paged_multi")
     return o, lse
 
 

@@ -23,7 +23,8 @@ ATTN_F32 = 1
 MAX_SPLITS = 256
 
 # Every symbol include/attn.h declares.
-EXPORTED = ("attn_prefill", "attn_prefill_paged", "attn_decode_paged", "attn_decode_workspace_bytes",
+EXPORTED = ("attn_prefill", "attn_prefill_paged", "attn_decode_paged", "attn_decode_paged_multi",
+            "attn_decode_workspace_bytes", "attn_decode_multi_workspace_bytes",
             "attn_decode_num_splits", "attn_status_string", "attn_abi_version")
 
 _lib = None
@@ -46,6 +47,10 @@ def _declare(lib):
     lib.attn_prefill_paged.restype = I
     lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, Z, P]
     lib.attn_decode_paged.restype = I
+    lib.attn_decode_paged_multi.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P, Z, P]
+    lib.attn_decode_paged_multi.restype = I
+    lib.attn_decode_multi_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.attn_decode_multi_workspace_bytes.restype = Z
     lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.attn_decode_workspace_bytes.restype = Z
     lib.attn_decode_num_splits.argtypes = [I, I, I, I, I]

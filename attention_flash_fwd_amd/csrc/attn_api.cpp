@@ -161,35 +161,45 @@ int attn_decode_num_splits(int batch, int n_kv_heads, int max_blocks_per_seq, in
     return resolve_splits(batch, n_kv_heads, max_blocks_per_seq, block_size, num_splits);
 }
 
+size_t attn_decode_multi_workspace_bytes(int batch, int seqlen_q, int n_q_heads, int n_kv_heads,
+                                         int head_dim, int max_blocks_per_seq, int block_size,
+                                         int num_splits)
+{
+    if (batch < 0 || seqlen_q <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0) return 0;
+    const int S = attn_decode_num_splits(batch, n_kv_heads, max_blocks_per_seq, block_size, num_splits);
+    if (S <= 0) return 0;
+    const int rows = batch * seqlen_q;
+    return part_o_bytes(rows, n_q_heads, head_dim, S) +
+           align_up((size_t)rows * n_q_heads * S * sizeof(float), 256);
+}
+
 size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
                                    int max_blocks_per_seq, int block_size, int num_splits)
 {
-    if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0) return 0;
-    const int S = attn_decode_num_splits(batch, n_kv_heads, max_blocks_per_seq, block_size, num_splits);
-    if (S <= 0) return 0;
-    return part_o_bytes(batch, n_q_heads, head_dim, S) +
-           align_up((size_t)batch * n_q_heads * S * sizeof(float), 256);
+    return attn_decode_multi_workspace_bytes(batch, 1, n_q_heads, n_kv_heads, head_dim,
+                                             max_blocks_per_seq, block_size, num_splits);
 }
 
-attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
-                                const int32_t *block_table, const int32_t *ctx_lens,
-                                void *o, float *lse,
-                                int batch, int n_q_heads, int n_kv_heads, int head_dim,
-                                int num_blocks, int block_size, int max_blocks_per_seq,
-                                int num_splits, float scale,
-                                void *workspace, size_t workspace_bytes,
-                                attn_stream_t stream)
+attn_status_t attn_decode_paged_multi(const void *q, const void *k_cache, const void *v_cache,
+                                      const int32_t *block_table, const int32_t *ctx_lens,
+                                      void *o, float *lse,
+                                      int batch, int seqlen_q, int n_q_heads, int n_kv_heads,
+                                      int head_dim, int num_blocks, int block_size,
+                                      int max_blocks_per_seq, int num_splits, float scale,
+                                      void *workspace, size_t workspace_bytes,
+                                      attn_stream_t stream)
 {
-    if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || num_blocks < 0 ||
-        max_blocks_per_seq < 0 || block_size <= 0)
+    if (batch < 0 || seqlen_q <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 ||
+        num_blocks < 0 || max_blocks_per_seq < 0 || block_size <= 0)
         return ATTN_ERR_SHAPE;
     if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_SHAPE;
     if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
     if (block_size != kBlockSize) return ATTN_ERR_UNSUPPORTED;
-    if (n_q_heads / n_kv_heads > 16) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)(n_q_heads / n_kv_heads) * seqlen_q > 16) return ATTN_ERR_UNSUPPORTED;
     if (num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_UNSUPPORTED;
     if ((long long)max_blocks_per_seq * block_size >= kMaxElems) return ATTN_ERR_SHAPE;
-    if ((long long)batch * n_q_heads * head_dim >= kMaxElems) return ATTN_ERR_SHAPE;
+    if ((long long)batch * seqlen_q * n_q_heads * head_dim >= kMaxElems) return ATTN_ERR_SHAPE;
+    if ((long long)block_size * n_kv_heads * head_dim * 2 >= (1LL << 31)) return ATTN_ERR_SHAPE;
     if (batch == 0) return ATTN_OK;
     if (q == nullptr || o == nullptr || block_table == nullptr || ctx_lens == nullptr)
         return ATTN_ERR_NULL;
@@ -200,8 +210,8 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
     if (lse != nullptr && !aligned(lse, 4)) return ATTN_ERR_ALIGN;
 
     const int S = resolve_splits(batch, n_kv_heads, max_blocks_per_seq, block_size, num_splits);
-    const size_t need = attn_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
-                                                    max_blocks_per_seq, block_size, num_splits);
+    const size_t need = attn_decode_multi_workspace_bytes(batch, seqlen_q, n_q_heads, n_kv_heads, head_dim,
+                                                          max_blocks_per_seq, block_size, num_splits);
     if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
 
@@ -213,10 +223,11 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
     a.ctx_lens = ctx_lens;
     a.part_o = static_cast<float *>(workspace);
     a.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                           part_o_bytes(batch, n_q_heads, head_dim, S));
+                                           part_o_bytes(batch * seqlen_q, n_q_heads, head_dim, S));
     a.o = static_cast<uint16_t *>(o);
     a.lse = lse;
     a.B = batch;
+    a.T = seqlen_q;
     a.Hq = n_q_heads;
     a.Hkv = n_kv_heads;
     a.num_blocks = num_blocks;
@@ -225,6 +236,21 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
     a.scale_log2 = scale * kLog2e;
     hipError_t e = attn::launch_decode(a, head_dim, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *block_table, const int32_t *ctx_lens,
+                                void *o, float *lse,
+                                int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                int num_blocks, int block_size, int max_blocks_per_seq,
+                                int num_splits, float scale,
+                                void *workspace, size_t workspace_bytes,
+                                attn_stream_t stream)
+{
+    return attn_decode_paged_multi(q, k_cache, v_cache, block_table, ctx_lens, o, lse, batch, 1,
+                                   n_q_heads, n_kv_heads, head_dim, num_blocks, block_size,
+                                   max_blocks_per_seq, num_splits, scale, workspace, workspace_bytes,
+                                   stream);
 }
 
 }  // extern "C"

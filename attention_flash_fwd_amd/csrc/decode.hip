@@ -7,23 +7,26 @@
 // reached through a block table).
 //
 // Kernel 1, decode_split: one workgroup of four waves per (chunk, KV head,
-//   sequence).  The G = Hq / Hkv query heads that share the KV head are the
-//   columns of the matrix-core products, so each K/V byte is read from HBM
-//   once for all of them.  The chunk's 16-token cache blocks are dealt
-//   round-robin to the waves.  Each wave streams its blocks with LDS-direct
-//   buffer loads into a private two-slot ring (the next block lands while
-//   the current one is computed) and keeps its own running max, running sum
-//   and partial output.  Per block:
-//     S^T (16 tokens x 16 heads)  = K Q^T        4 x 16x16x32 bf16 MFMA
+//   sequence).  The G = Hq / Hkv query heads that share the KV head, times
+//   the T new tokens of the sequence (T = 1 for plain decode, several for
+//   speculative verification), are the columns of the matrix-core products,
+//   so each K/V byte is read from HBM once for all of them.  The chunk's
+//   16-token cache blocks are dealt round-robin to the waves.  Each wave
+//   streams its blocks with LDS-direct buffer loads into a private two-slot
+//   ring (the next block lands while the current one is computed) and keeps
+//   its own running max, running sum and partial output.  Per block:
+//     S^T (16 tokens x 16 columns) = K Q^T   4 x 16x16x32 bf16 MFMA
 //     P = 2^(S - m), lazy rescale of (l, O) when the max grows by > 2^8
-//     O^T (D x 16 heads)         += V^T P^T      D/16 x 16x16x16 bf16 MFMA
+//     O^T (D x 16 columns)       += V^T P^T  D/16 x 16x16x16 bf16 MFMA
+//   New token t sees the keys up to position ctx - T + t; that limit is only
+//   checked on the blocks that reach past ctx - T.
 //   The score accumulator of a lane (4 tokens of one head) is exactly the
 //   B operand the 16x16x16 product wants, and the V^T operand comes from one
 //   transposing LDS read per 16 rows of d.  Cache slots past the chunk end
 //   are never fetched (their buffer offsets fall outside the block and read
 //   as zero).  The four wave partials are merged in LDS and the chunk's
 //   normalised output and log-sum-exp are written as fp32.
-// Kernel 2, decode_combine: one workgroup per (sequence, query head) merges
+// Kernel 2, decode_combine: one workgroup per (sequence, token, query head) merges
 //   the chunk partials: M = max lse_s, w_s = e^(lse_s - M),
 //   O = sum w_s O_s / sum w_s, lse = M + ln sum w_s; O rounded to bf16.
 #include "gfx950.hpp"
@@ -92,8 +95,12 @@ __device__ __forceinline__ void issue_block(const uint16_t *kc, const uint16_t *
 }
 
 // One block from a slot: scores, online softmax, PV.
+// Tokens 4 g + v of the block at or past `valid` are masked; with `causal`
+// set, so is every token past `lim` (absolute position) for this lane's
+// column (the causal limit of its query among several new tokens).
 template <int D>
 __device__ __forceinline__ void compute_block(const uint8_t *ks, const uint8_t *vs, int valid,
+                                              bool causal, int tok0, int lim,
                                               float scale_log2, int l16, int g, WaveState<D> &w)
 {
     using Gm = Geom<D>;
@@ -111,7 +118,8 @@ __device__ __forceinline__ void compute_block(const uint8_t *ks, const uint8_t *
     float mx = kNegInf;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-        const float t = (4 * g + v < valid) ? s[v] * scale_log2 : kNegInf;
+        const bool vis = 4 * g + v < valid && (!causal || tok0 + 4 * g + v <= lim);
+        const float t = vis ? s[v] * scale_log2 : kNegInf;
         s[v] = t;
         mx = fmaxf(mx, t);
     }
@@ -167,6 +175,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     const int hk = (blockIdx.x / a.splits) % a.Hkv;
     const int b = blockIdx.x / (a.splits * a.Hkv);
     const int G = a.Hq / a.Hkv;
+    const int T = a.T;                  // new tokens per sequence
+    const int GT = G * T;               // matrix-core columns in use: (token, head) pairs
 
     // Sequence length through the scalar cache: everything derived from it
     // (chunk bounds, trip counts) stays wave-uniform.
@@ -186,9 +196,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
 
     WaveState<D> w;
     {
-        // Columns past G read head G - 1 and are zeroed (no branch around the load).
-        const bool hv = l16 < G;
-        const uint16_t *qp = a.q + ((size_t)b * a.Hq + hk * G + min(l16, G - 1)) * D + 8 * g;
+        // Column col = t G + g holds query head hk G + g of new token t.
+        // Columns past G T read the last valid one and are zeroed (no branch
+        // around the load).
+        const bool hv = l16 < GT;
+        const int col = min(l16, GT - 1);
+        const uint16_t *qp = a.q + (((size_t)b * T + col / G) * a.Hq + hk * G + col % G) * D + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             const u32x4_t x = *reinterpret_cast<const u32x4_t *>(qp + 32 * kk);
@@ -242,16 +255,22 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     auto valid_rows = [&](int j) __attribute__((always_inline)) {
         return min(kBS, t_end - (blk0 + wave + kWaves * j) * kBS);
     };
+    // New token t sees keys up to position ctx - T + t; only blocks reaching
+    // past ctx - T need that check.
+    const int lim = ctx - T + (l16 < GT ? l16 / G : 0);
+    auto tok0_of = [&](int j) __attribute__((always_inline)) { return (blk0 + wave + kWaves * j) * kBS; };
+    auto causal_blk = [&](int j) __attribute__((always_inline)) { return T > 1 && tok0_of(j) + kBS - 1 > ctx - T; };
 
     // Every path through the loop issues the same loads in the same order,
     // so the wait before each slot's reads is exact.
     issue(0, k_s0[wave], v_s0[wave]);
     issue(1, k_s1[wave], v_s1[wave]);
     for (int j = 0; j < nmine; j += 2) {
-        compute_block<D>(k_s0[wave], v_s0[wave], valid_rows(j), a.scale_log2, l16, g, w);
+        compute_block<D>(k_s0[wave], v_s0[wave], valid_rows(j), causal_blk(j), tok0_of(j), lim, a.scale_log2, l16, g, w);
         issue(j + 2, k_s0[wave], v_s0[wave]);
         if (j + 1 < nmine)
-            compute_block<D>(k_s1[wave], v_s1[wave], valid_rows(j + 1), a.scale_log2, l16, g, w);
+            compute_block<D>(k_s1[wave], v_s1[wave], valid_rows(j + 1), causal_blk(j + 1), tok0_of(j + 1), lim,
+                             a.scale_log2, l16, g, w);
         issue(j + 3, k_s1[wave], v_s1[wave]);
     }
 
@@ -275,8 +294,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
         *reinterpret_cast<f32x4_t *>(mo + l16 * D + 16 * db + 4 * g) = w.o[db];
     __syncthreads();
 
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-        const int head = idx / D, d = idx % D;
+    for (int idx = threadIdx.x; idx < GT * D; idx += kThreads) {
+        const int head = idx / D, d = idx % D;      // head = matrix-core column
         float M = kNegInf;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) M = fmaxf(M, ml[v * 16 + head]);
@@ -292,7 +311,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
                 O += src[head * D + d] * sc;
             }
         }
-        const size_t row = ((size_t)b * a.Hq + hk * G + head) * a.splits + split;
+        const size_t row = (((size_t)b * T + head / G) * a.Hq + hk * G + head % G) * a.splits + split;
         float o_out = L > 0.f ? O / L : 0.f;
         float lse_out = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
         if (any_bad) {
@@ -316,7 +335,7 @@ __global__ void __launch_bounds__(kThreads) decode_combine_kernel(DecodeArgs a)
     __shared__ f32x4_t red[SUB][TPR];
     __shared__ float stat[3];
 
-    const int row = blockIdx.x;                // b * Hq + hq
+    const int row = blockIdx.x;                // (b * T + t) * Hq + hq
     const int t = threadIdx.x, sub = t / TPR, c = t % TPR;
     const int S = a.splits;
     const float *plse = a.part_lse + (size_t)row * S;
@@ -380,8 +399,11 @@ __global__ void __launch_bounds__(kThreads) decode_combine_kernel(DecodeArgs a)
         const u32x2_t packed = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
         *reinterpret_cast<u32x2_t *>(a.o + (size_t)row * D + 4 * t) = packed;
     }
-    if (a.lse != nullptr && t == 0)
-        a.lse[row] = nan ? __builtin_nanf("") : (wsum > 0.f ? M + logf(wsum) : kNegInf);
+    if (a.lse != nullptr && t == 0) {
+        const int th = row % (a.T * a.Hq);     // lse is [B, Hq, T]
+        const size_t li = ((size_t)(row / (a.T * a.Hq)) * a.Hq + th % a.Hq) * a.T + th / a.Hq;
+        a.lse[li] = nan ? __builtin_nanf("") : (wsum > 0.f ? M + logf(wsum) : kNegInf);
+    }
 }
 
 template <int D>
@@ -392,7 +414,7 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
     hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)g1), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.B * a.Hq)), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.B * a.T * a.Hq)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -21,16 +21,16 @@ struct PrefillArgs {
 };
 
 struct DecodeArgs {
-    const uint16_t *q;            // [B,Hq,D] bf16
+    const uint16_t *q;            // [B,T,Hq,D] bf16 (T new tokens per sequence)
     const uint16_t *k_cache;      // [num_blocks,16,Hkv,D] bf16
     const uint16_t *v_cache;
     const int32_t *block_table;   // [B,max_blocks]
     const int32_t *ctx_lens;      // [B]
-    float *part_o;                // [B,Hq,splits,D] fp32
-    float *part_lse;              // [B,Hq,splits]   fp32
-    uint16_t *o;                  // [B,Hq,D] bf16
-    float *lse;                   // [B,Hq] or nullptr
-    int B, Hq, Hkv, num_blocks, max_blocks, splits;
+    float *part_o;                // [B,T,Hq,splits,D] fp32
+    float *part_lse;              // [B,T,Hq,splits]   fp32
+    uint16_t *o;                  // [B,T,Hq,D] bf16
+    float *lse;                   // [B,Hq,T] or nullptr
+    int B, T, Hq, Hkv, num_blocks, max_blocks, splits;
     float scale_log2;
 };
 

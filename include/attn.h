@@ -215,13 +215,55 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
                                 void *workspace, size_t workspace_bytes,
                                 attn_stream_t stream);
 
+/*
+ * attn_decode_paged_multi -- seqlen_q new query tokens per sequence over a
+ * paged KV cache that already holds their keys: the verification step of
+ * speculative decoding, where the draft tokens are checked in one pass
+ * ("推理加速" interview notes, section speculative decoding: the target
+ * model checks several draft tokens at once; "GPU Kernel 调度：大模型推理的
+ * 拐点 2026", paragraph on the coupling of speculative decoding with
+ * Flash-Decoding).  Same split-KV scheme and partial merge as
+ * attn_decode_paged; the seqlen_q tokens share every K/V read.
+ *
+ *   q            [batch, seqlen_q, n_q_heads, head_dim]             bf16
+ *   o            [batch, seqlen_q, n_q_heads, head_dim]             bf16, written
+ *   lse          [batch, n_q_heads, seqlen_q] fp32, written; may be NULL
+ *   workspace    attn_decode_multi_workspace_bytes(...) bytes, 256-byte aligned
+ *   other arguments as for attn_decode_paged.
+ *
+ * Token t (0-based) of sequence b sits at position ctx_lens[b] - seqlen_q + t
+ * and sees the keys at positions <= ctx_lens[b] - seqlen_q + t (causal among
+ * the new tokens; the result equals attn_prefill_paged with the same
+ * arguments).  A token with no visible key gets O = 0, lse = -inf.
+ * Supported: (n_q_heads / n_kv_heads) * seqlen_q <= 16, plus the limits of
+ * attn_decode_paged; seqlen_q == 1 is attn_decode_paged.
+ */
+attn_status_t attn_decode_paged_multi(const void *q, const void *k_cache, const void *v_cache,
+                                      const int32_t *block_table, const int32_t *ctx_lens,
+                                      void *o, float *lse,
+                                      int batch, int seqlen_q, int n_q_heads, int n_kv_heads,
+                                      int head_dim, int num_blocks, int block_size,
+                                      int max_blocks_per_seq, int num_splits, float scale,
+                                      void *workspace, size_t workspace_bytes,
+                                      attn_stream_t stream);
+
+/*
+ * attn_decode_multi_workspace_bytes -- workspace of attn_decode_paged_multi:
+ * partial outputs [batch, seqlen_q, n_q_heads, splits, head_dim] fp32, then
+ * their log-sum-exps [batch, seqlen_q, n_q_heads, splits] fp32.  Returns 0
+ * for invalid arguments.
+ */
+size_t attn_decode_multi_workspace_bytes(int batch, int seqlen_q, int n_q_heads, int n_kv_heads,
+                                         int head_dim, int max_blocks_per_seq, int block_size,
+                                         int num_splits);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *attn_status_string(attn_status_t status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int attn_abi_version(void);
 
-#define ATTN_ABI_VERSION ((1 << 16) | 1)
+#define ATTN_ABI_VERSION ((1 << 16) | 2)
 
 #ifdef __cplusplus
 }

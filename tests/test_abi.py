@@ -59,7 +59,7 @@ def test_exports_are_c_symbols():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.attn_abi_version() == (1 << 16) | 1
+    assert lib.attn_abi_version() == (1 << 16) | 2
     for code in range(8):
         s = lib.attn_status_string(code).decode()
         assert s and s != "unknown status"
@@ -153,6 +153,30 @@ def test_prefill_paged_validation(lib):
     assert prefill_paged(lib, lse=FAKE + 2) == ALIGN
     assert prefill_paged(lib, B=0, q=0, o=0, tbl=0, ctx=0) == OK
     assert prefill_paged(lib, Sq=0, q=0, o=0, tbl=0, ctx=0) == OK
+
+
+def decode_multi(lib, T=2, q=FAKE, ws=FAKE, B=2, Hq=8, Hkv=2, D=128, max_blocks=5, splits=4, ws_bytes=None,
+                 **kw):
+    P = ctypes.c_void_p
+    if ws_bytes is None:
+        ws_bytes = lib.attn_decode_multi_workspace_bytes(B, T, Hq, Hkv, D, max_blocks, 16, splits)
+    return lib.attn_decode_paged_multi(P(q), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), B, T,
+                                       Hq, Hkv, D, 10, 16, max_blocks, splits, 0.1, P(ws), ws_bytes, P(0))
+
+
+def test_decode_multi_validation(lib):
+    assert decode_multi(lib, T=0) == SHAPE
+    assert decode_multi(lib, T=5, Hq=8, Hkv=2) == UNSUP     # 4 heads x 5 tokens > 16 columns
+    assert decode_multi(lib, T=2, Hq=16, Hkv=1) == UNSUP
+    assert decode_multi(lib, T=4, q=FAKE_MIS) == ALIGN
+    assert decode_multi(lib, T=4, ws=0) == WORKSPACE
+    need = lib.attn_decode_multi_workspace_bytes(2, 4, 8, 2, 128, 5, 16, 4)
+    assert decode_multi(lib, T=4, ws_bytes=need - 1) == WORKSPACE
+    # The workspace holds one partial per (sequence, token, head, split).
+    assert need >= 2 * 4 * 8 * 4 * 129 * 4
+    assert lib.attn_decode_multi_workspace_bytes(2, 1, 8, 2, 128, 5, 16, 4) == \
+        lib.attn_decode_workspace_bytes(2, 8, 2, 128, 5, 16, 4)
+    assert lib.attn_decode_multi_workspace_bytes(2, 0, 8, 2, 128, 5, 16, 4) == 0
 
 
 def test_workspace_and_split_rules(lib):

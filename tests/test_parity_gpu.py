@@ -427,3 +427,41 @@ def test_prefill_paged_long_chunk_sampled(afa):
     got_l = np.array([lse[b, h, i].item() for (b, h, i) in rows])
     check_o(got, o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
     check_lse(got_l, l_ref, BF16_LSE_ABS)
+
+
+# ------------------------------------------------------ multi-token decode ---
+@pytest.mark.parametrize("ctx,T,Hq,Hkv,D,splits", [
+    ([300, 77, 1000, 5], 4, 8, 2, 128, 4),      # G*T = 16; ctx 5 > T
+    ([2, 700], 3, 8, 2, 128, 3),                # ctx < T: the first token sees nothing
+    ([513, 2049], 2, 64, 8, 128, 16),           # the long-context head layout, T = 2
+    ([129, 4000], 8, 16, 8, 128, 0),            # G = 2, T = 8, automatic splits
+    ([390, 45], 4, 8, 2, 64, 5),                # D = 64
+])
+def test_decode_multi_matches_oracle_and_chunked_prefill(afa, ctx, T, Hq, Hkv, D, splits):
+    say(f"case decode_multi ctx{ctx} T{T} Hq{Hq} Hkv{Hkv} D{D} splits{splits}")
+    inp, q = gen_paged_prefill(ctx, T, Hq, Hkv, D, seed=sum(ctx) * 3 + T, spare_blocks=2)
+    scale = 1 / math.sqrt(D)
+    o, lse = afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                    num_splits=splits, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = paged_prefill_oracle(inp, q, True, scale)
+    check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse), l_ref, BF16_LSE_ABS)
+    # Same computation as the chunked-prefill entry point (different kernel).
+    o_p, l_p = afa.prefill_paged(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                 causal=True, scale=scale)
+    torch.cuda.synchronize()
+    assert (o.float() - o_p.float()).abs().max().item() <= 2e-2
+    fin = torch.isfinite(l_p)
+    assert torch.equal(fin, torch.isfinite(lse))
+    assert (lse[fin] - l_p[fin]).abs().max().item() <= 1e-4
+
+
+def test_decode_multi_single_token_is_decode(afa):
+    say("case decode_multi T=1 == decode_paged")
+    inp = gen_decode([1000, 37, 4097], 32, 8, 128, seed=5)
+    o1, l1 = afa.decode_paged(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens, num_splits=8)
+    o2, l2 = afa.decode_paged_multi(inp.q[:, None].contiguous(), inp.k_cache, inp.v_cache,
+                                    inp.block_table, inp.ctx_lens, num_splits=8)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2[:, 0]) and torch.equal(l1, l2[:, :, 0])
