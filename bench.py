@@ -31,6 +31,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
 PEAK_HBM_BPS = 8.0e12         # MI355X HBM3E
 COPY_BYTES = 1 << 30          # calibration copy (profiling runs only)
+# Workloads beyond the hot path's step, timed on their own after it (never
+# part of `value` or `ms_per_step`).
+EXTRAS = ("chunked_prefill", "decode_multi")
+MULTI_T = 4                   # new tokens per sequence in the multi-token decode extra
 METRIC = "prefill attn TFLOP/s + decode KV GB/s, % of MI355X bf16/HBM peak"
 
 
@@ -40,7 +44,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--parts", default="prefill,decode_b64,decode_128k",
+    p.add_argument("--parts", default="prefill,decode_b64,decode_128k," + ",".join(EXTRAS),
                    help="comma-separated subset (for profiling runs); 'copy' adds a plain "
                         "1 GiB device-to-device copy that calibrates the HBM byte counters")
     return p.parse_args()
@@ -175,6 +179,23 @@ def main():
         o = torch.empty_like(inp.q)
         lse = torch.empty(inp.q.shape[:2], dtype=torch.float32, device=dev)
         dec[name] = (cfg, inp, ws, o, lse)
+    extra_in = {}
+    if "chunked_prefill" in parts:
+        cp = inputs.CHUNKED_PREFILL
+        cinp = inputs.decode_inputs([cp.ctx] * cp.batch, cp.n_q_heads, cp.n_kv_heads, cp.head_dim,
+                                    seed=cp.seed, device=dev)
+        cq = inputs.chunk_queries(cp.batch, cp.chunk, cp.n_q_heads, cp.head_dim, seed=cp.seed, device=dev)
+        co = torch.empty_like(cq)
+        clse = torch.empty((cp.batch, cp.n_q_heads, cp.chunk), dtype=torch.float32, device=dev)
+        extra_in["chunked_prefill"] = (cp, cinp, cq, co, clse)
+    if "decode_multi" in parts:
+        mcfg = inputs.DECODE_B64
+        minp = inputs.decode_config_inputs(mcfg, device=dev)
+        mq = inputs.chunk_queries(mcfg.batch, MULTI_T, mcfg.n_q_heads, mcfg.head_dim, seed=mcfg.seed, device=dev)
+        mws = afa.decode_workspace(mq, minp.k_cache, minp.block_table, mcfg.num_splits)
+        mo = torch.empty_like(mq)
+        mlse = torch.empty((mcfg.batch, mcfg.n_q_heads, MULTI_T), dtype=torch.float32, device=dev)
+        extra_in["decode_multi"] = (mcfg, minp, mq, mws, mo, mlse)
     if pf_in is not None:
         q, k, v = pf_in
         pf_o = torch.empty_like(q)
@@ -199,8 +220,25 @@ def main():
     for name in dec:
         runners.append((name, lambda n=name: run_decode(n)))
 
+    def run_chunked():
+        cp, cinp, cq, co, clse = extra_in["chunked_prefill"]
+        afa.prefill_paged(cq, cinp.k_cache, cinp.v_cache, cinp.block_table, cinp.ctx_lens, causal=True,
+                          scale=cp.scale, out=co, lse_out=clse)
+
+    def run_multi():
+        mcfg, minp, mq, mws, mo, mlse = extra_in["decode_multi"]
+        afa.decode_paged_multi(mq, minp.k_cache, minp.v_cache, minp.block_table, minp.ctx_lens,
+                               num_splits=mcfg.num_splits, scale=mcfg.scale, out=mo, lse_out=mlse,
+                               workspace=mws)
+
+    extra_runners = []
+    if "chunked_prefill" in extra_in:
+        extra_runners.append(("chunked_prefill", run_chunked))
+    if "decode_multi" in extra_in:
+        extra_runners.append(("decode_multi", run_multi))
+
     for _ in range(args.warmup):
-        for _, fn in runners:
+        for _, fn in runners + extra_runners:
             fn()
     torch.cuda.synchronize()
 
@@ -226,6 +264,31 @@ def main():
     ms_per_step = total_ms / args.steps
 
     part_ms = {name: sum(a.elapsed_time(b) for a, b in ev[name]) / args.steps for name, _ in runners}
+
+    # ---- extras: timed on their own, after the step ----------------------
+    extras = {}
+    for name, fn in extra_runners:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a_ev, b_ev in evs:
+            a_ev.record(stream)
+            fn()
+            b_ev.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(a_ev.elapsed_time(b_ev) for a_ev, b_ev in evs) / args.steps
+        if name == "chunked_prefill":
+            cp = extra_in[name][0]
+            tf = cp.flops() / (ms * 1e-3) / 1e12
+            extras[name] = {"workload": cp.name, "ms": ms, "tflops": tf,
+                            "frac_of_peak": tf * 1e12 / PEAK_BF16_FLOPS, "flops": cp.flops()}
+        elif name == "decode_multi":
+            mcfg, minp, mq = extra_in[name][:3]
+            nb = decode_bytes(minp, mcfg.n_q_heads) + 2 * (MULTI_T - 1) * mq[:, 0].numel() * 2
+            gbps = nb / (ms * 1e-3) / 1e9
+            extras[name] = {"workload": f"{mcfg.name}_T{MULTI_T}", "ms": ms, "gbps": gbps,
+                            "frac_of_peak": gbps * 1e9 / PEAK_HBM_BPS, "bytes": nb,
+                            "num_splits": mcfg.num_splits}
     out_parts = {}
     sol_ms = 0.0
     if pf_in is not None:
@@ -287,6 +350,7 @@ def main():
         "parts": out_parts,
         "roofline": roofline,
         "roofline_decode": decode_roofline,
+        "extras": extras,
         "cpu_baseline": cpu,
         "wall_s_timed_region": wall,
     }
