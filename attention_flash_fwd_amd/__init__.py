@@ -173,6 +173,43 @@ def decode_paged_multi(q, k_cache, v_cache, block_table, ctx_lens, num_splits: i
     return o, lse
 
 
+def decode_paged_fp8(q, k_cache, v_cache, block_table, ctx_lens, k_scale: float, v_scale: float,
+                     num_splits: int = 0, scale: float | None = None, out=None, lse_out=None,
+                     workspace=None, return_lse: bool = True):
+    """Decode over an FP8 (OCP e4m3) paged KV cache with per-tensor scales:
+    K = e4m3(k_cache) * k_scale, V = e4m3(v_cache) * v_scale.  q [B,Hq,D] (one
+    token) or [B,T,Hq,D]; caches uint8 [num_blocks,16,Hkv,D] holding e4m3
+    codes.  Returns (o, lse) shaped like decode_paged / decode_paged_multi."""
+    import torch
+    lib = _lib.load()
+    _need_gpu(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out, workspace)
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise TypeError("decode_paged_fp8 takes bf16 q and uint8 (e4m3) caches")
+    if block_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
+        raise TypeError("block_table and ctx_lens must be int32")
+    single = q.dim() == 3
+    q4 = q[:, None] if single else q
+    B, T, Hq, D = q4.shape
+    nblocks, bs, Hkv, Dk = k_cache.shape
+    if Dk != D or v_cache.shape != k_cache.shape or block_table.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("inconsistent decode shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = decode_workspace(q4, k_cache, block_table, num_splits)
+    o = out if out is not None else torch.empty_like(q)
+    lse = lse_out
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq) if single else (B, Hq, T), dtype=torch.float32, device=q.device)
+    st = lib.attn_decode_paged_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                   _ptr(ctx_lens), _ptr(o), _ptr(lse), B, T, Hq, Hkv, D, nblocks, bs,
+                                   block_table.shape[1], int(num_splits), float(scale), float(k_scale),
+                                   float(v_scale), _ptr(workspace), workspace.numel(), _stream_handle(q))
+    if st != _lib.ATTN_OK:
+        raise AttnError(st, "attn_decode_paged_fp8")
+    return o, lse
+
+
 def decode_paged(q, k_cache, v_cache, block_table, ctx_lens, num_splits: int = 0,
                  scale: float | None = None, out=None, lse_out=None, workspace=None,
                  return_lse: bool = True):

@@ -24,6 +24,7 @@ MAX_SPLITS = 256
 
 # Every symbol include/attn.h declares.
 EXPORTED = ("attn_prefill", "attn_prefill_paged", "attn_decode_paged", "attn_decode_paged_multi",
+            "attn_decode_paged_fp8",
             "attn_decode_workspace_bytes", "attn_decode_multi_workspace_bytes",
             "attn_decode_num_splits", "attn_status_string", "attn_abi_version")
 
@@ -49,6 +50,8 @@ def _declare(lib):
     lib.attn_decode_paged.restype = I
     lib.attn_decode_paged_multi.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P, Z, P]
     lib.attn_decode_paged_multi.restype = I
+    lib.attn_decode_paged_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, F, F, P, Z, P]
+    lib.attn_decode_paged_fp8.restype = I
     lib.attn_decode_multi_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
     lib.attn_decode_multi_workspace_bytes.restype = Z
     lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, I]

@@ -180,14 +180,17 @@ size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
                                              max_blocks_per_seq, block_size, num_splits);
 }
 
-attn_status_t attn_decode_paged_multi(const void *q, const void *k_cache, const void *v_cache,
-                                      const int32_t *block_table, const int32_t *ctx_lens,
-                                      void *o, float *lse,
-                                      int batch, int seqlen_q, int n_q_heads, int n_kv_heads,
-                                      int head_dim, int num_blocks, int block_size,
-                                      int max_blocks_per_seq, int num_splits, float scale,
-                                      void *workspace, size_t workspace_bytes,
-                                      attn_stream_t stream)
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by the three paged-decode entry points.
+attn_status_t decode_common(const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_table, const int32_t *ctx_lens, void *o, float *lse,
+                            int batch, int seqlen_q, int n_q_heads, int n_kv_heads, int head_dim,
+                            int num_blocks, int block_size, int max_blocks_per_seq, int num_splits,
+                            float scale, bool kv_fp8, float k_scale, float v_scale,
+                            void *workspace, size_t workspace_bytes, attn_stream_t stream)
 {
     if (batch < 0 || seqlen_q <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 ||
         num_blocks < 0 || max_blocks_per_seq < 0 || block_size <= 0)
@@ -197,6 +200,7 @@ attn_status_t attn_decode_paged_multi(const void *q, const void *k_cache, const 
     if (block_size != kBlockSize) return ATTN_ERR_UNSUPPORTED;
     if ((long long)(n_q_heads / n_kv_heads) * seqlen_q > 16) return ATTN_ERR_UNSUPPORTED;
     if (num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_UNSUPPORTED;
+    if (kv_fp8 && !(std::isfinite(k_scale) && std::isfinite(v_scale))) return ATTN_ERR_SHAPE;
     if ((long long)max_blocks_per_seq * block_size >= kMaxElems) return ATTN_ERR_SHAPE;
     if ((long long)batch * seqlen_q * n_q_heads * head_dim >= kMaxElems) return ATTN_ERR_SHAPE;
     if ((long long)block_size * n_kv_heads * head_dim * 2 >= (1LL << 31)) return ATTN_ERR_SHAPE;
@@ -217,8 +221,8 @@ attn_status_t attn_decode_paged_multi(const void *q, const void *k_cache, const 
 
     attn::DecodeArgs a;
     a.q = static_cast<const uint16_t *>(q);
-    a.k_cache = static_cast<const uint16_t *>(k_cache);
-    a.v_cache = static_cast<const uint16_t *>(v_cache);
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
     a.block_table = block_table;
     a.ctx_lens = ctx_lens;
     a.part_o = static_cast<float *>(workspace);
@@ -233,9 +237,43 @@ attn_status_t attn_decode_paged_multi(const void *q, const void *k_cache, const 
     a.num_blocks = num_blocks;
     a.max_blocks = max_blocks_per_seq;
     a.splits = S;
-    a.scale_log2 = scale * kLog2e;
-    hipError_t e = attn::launch_decode(a, head_dim, static_cast<hipStream_t>(stream));
+    a.scale_log2 = scale * (kv_fp8 ? k_scale : 1.0f) * kLog2e;
+    a.v_scale = kv_fp8 ? v_scale : 1.0f;
+    hipError_t e = attn::launch_decode(a, head_dim, kv_fp8, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_decode_paged_multi(const void *q, const void *k_cache, const void *v_cache,
+                                      const int32_t *block_table, const int32_t *ctx_lens,
+                                      void *o, float *lse,
+                                      int batch, int seqlen_q, int n_q_heads, int n_kv_heads,
+                                      int head_dim, int num_blocks, int block_size,
+                                      int max_blocks_per_seq, int num_splits, float scale,
+                                      void *workspace, size_t workspace_bytes,
+                                      attn_stream_t stream)
+{
+    return decode_common(q, k_cache, v_cache, block_table, ctx_lens, o, lse, batch, seqlen_q, n_q_heads,
+                         n_kv_heads, head_dim, num_blocks, block_size, max_blocks_per_seq, num_splits,
+                         scale, false, 1.0f, 1.0f, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_decode_paged_fp8(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_table, const int32_t *ctx_lens,
+                                    void *o, float *lse,
+                                    int batch, int seqlen_q, int n_q_heads, int n_kv_heads,
+                                    int head_dim, int num_blocks, int block_size,
+                                    int max_blocks_per_seq, int num_splits, float scale,
+                                    float k_scale, float v_scale,
+                                    void *workspace, size_t workspace_bytes,
+                                    attn_stream_t stream)
+{
+    return decode_common(q, k_cache, v_cache, block_table, ctx_lens, o, lse, batch, seqlen_q, n_q_heads,
+                         n_kv_heads, head_dim, num_blocks, block_size, max_blocks_per_seq, num_splits,
+                         scale, true, k_scale, v_scale, workspace, workspace_bytes, stream);
 }
 
 attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,

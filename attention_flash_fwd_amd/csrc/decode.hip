@@ -49,18 +49,22 @@ __device__ __forceinline__ f32x4_t mfma_16x16x16_bf16(u32x2_t a, u32x2_t b, f32x
                                                      __builtin_bit_cast(bf16x4_t, b), c, 0, 0, 0);
 }
 
-// One cache block of one KV head in LDS: 16 token rows of D bf16.  16-byte
-// chunk c of row r holds global chunk c ^ swz(r), which keeps both the
-// row-wise K reads and the transposing V reads free of bank conflicts.
-template <int D>
+// One cache block of one KV head in LDS: 16 token rows of D elements of EB
+// bytes (2: bf16, 1: fp8 e4m3).  16-byte chunk c of row r holds global chunk
+// c ^ swz(r), which keeps the row-wise K reads (16 bytes per lane for bf16, 8
+// for fp8) and the transposing V reads free of bank conflicts.
+template <int D, int EB = 2>
 struct Geom {
-    static constexpr int row_bytes = 2 * D;
+    static constexpr int row_bytes = EB * D;
     static constexpr int rows_per_load = 1024 / row_bytes;   // rows one wave-wide DMA fills
     static constexpr int loads = kBS / rows_per_load;        // DMAs per block of K (or V)
     static constexpr int slot_bytes = kBS * row_bytes;
     __device__ static __forceinline__ int swz(int r)
     {
-        return D == 128 ? (((r << 1) | (r >> 3)) & 15) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+        if constexpr (EB == 2)
+            return D == 128 ? (((r << 1) | (r >> 3)) & 15) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+        else   // rows of 128 or 64 bytes: spread the rows that share banks over the chunks
+            return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
     }
 };
 
@@ -75,12 +79,11 @@ struct WaveState {
 // Queue the K and V of one block into a slot.  `valid` rows (tokens) are
 // fetched, the rest read as zero; voff[i] is this lane's offset in the block
 // for its row of DMA i.
-template <int D>
-__device__ __forceinline__ void issue_block(const uint16_t *kc, const uint16_t *vc, long long phys,
-                                            uint32_t blk_bytes, int valid, const uint32_t (&voff)[Geom<D>::loads],
+template <class Gm>
+__device__ __forceinline__ void issue_block(const void *kc, const void *vc, long long phys,
+                                            uint32_t blk_bytes, int valid, const uint32_t (&voff)[Gm::loads],
                                             int lane, uint8_t *ks, uint8_t *vs)
 {
-    using Gm = Geom<D>;
     const char *kb = reinterpret_cast<const char *>(kc) + phys * blk_bytes;
     const char *vb = reinterpret_cast<const char *>(vc) + phys * blk_bytes;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, blk_bytes);
@@ -98,19 +101,60 @@ __device__ __forceinline__ void issue_block(const uint16_t *kc, const uint16_t *
 // Tokens 4 g + v of the block at or past `valid` are masked; with `causal`
 // set, so is every token past `lim` (absolute position) for this lane's
 // column (the causal limit of its query among several new tokens).
+// Four e4m3 values -> four bf16 (exact: every e4m3 value is a bf16 value).
+__device__ __forceinline__ u32x2_t fp8x4_to_bf16(uint32_t x)
+{
+    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
+    return u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+// Convert this wave's fp8 V block (slot layout Geom<D,1>) to bf16 in the
+// scratch block cv (layout Geom<D,2>): lane L handles row L / 4, a quarter
+// of its elements.
 template <int D>
+__device__ __forceinline__ void convert_v(const uint8_t *vs, uint8_t *cv, int lane)
+{
+    using G8 = Geom<D, 1>;
+    using G16 = Geom<D, 2>;
+    constexpr int CH = D / 64;                   // fp8 chunks (16 values) per lane
+    const int r = lane >> 2, q4 = lane & 3;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int gc = q4 * CH + i;              // fp8 chunk: values 16 gc .. 16 gc + 15
+        const u32x4_t x = *reinterpret_cast<const u32x4_t *>(vs + r * G8::row_bytes + ((gc ^ G8::swz(r)) << 4));
+        const u32x2_t a0 = fp8x4_to_bf16(x[0]), a1 = fp8x4_to_bf16(x[1]);
+        const u32x2_t a2 = fp8x4_to_bf16(x[2]), a3 = fp8x4_to_bf16(x[3]);
+        const u32x4_t lo = {a0[0], a0[1], a1[0], a1[1]}, hi = {a2[0], a2[1], a3[0], a3[1]};
+        *reinterpret_cast<u32x4_t *>(cv + r * G16::row_bytes + (((2 * gc) ^ G16::swz(r)) << 4)) = lo;
+        *reinterpret_cast<u32x4_t *>(cv + r * G16::row_bytes + (((2 * gc + 1) ^ G16::swz(r)) << 4)) = hi;
+    }
+}
+
+// One block: scores, online softmax, PV.  ks holds K with EB-byte elements;
+// vs holds V as bf16 (for fp8 caches, the converted scratch copy).
+template <int D, int EB>
 __device__ __forceinline__ void compute_block(const uint8_t *ks, const uint8_t *vs, int valid,
                                               bool causal, int tok0, int lim,
                                               float scale_log2, int l16, int g, WaveState<D> &w)
 {
-    using Gm = Geom<D>;
+    using Gm = Geom<D, 2>;
+    using GK = Geom<D, EB>;
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
     {
-        const uint8_t *row = ks + l16 * Gm::row_bytes;
-        const int sw = Gm::swz(l16);
+        const uint8_t *row = ks + l16 * GK::row_bytes;
+        const int sw = GK::swz(l16);
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
-            const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(row + (((4 * kk + g) ^ sw) << 4));
+            u32x4_t kf;
+            if constexpr (EB == 2) {
+                kf = *reinterpret_cast<const u32x4_t *>(row + (((4 * kk + g) ^ sw) << 4));
+            } else {
+                // d = 32 kk + 8 g .. +8: 8 bytes of fp8 chunk 2 kk + g / 2.
+                const u32x2_t x = *reinterpret_cast<const u32x2_t *>(row + (((2 * kk + (g >> 1)) ^ sw) << 4) + ((g & 1) << 3));
+                const u32x2_t lo = fp8x4_to_bf16(x[0]), hi = fp8x4_to_bf16(x[1]);
+                kf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+            }
             s = mfma_16x16x32_bf16(kf, w.qf[kk], s);
         }
     }
@@ -156,16 +200,19 @@ __device__ __forceinline__ void compute_block(const uint8_t *ks, const uint8_t *
     }
 }
 
-template <int D>
+template <int D, int EB>
 __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
 {
-    using Gm = Geom<D>;
+    using Gm = Geom<D, EB>;
     // Two ring slots per wave, K and V each in an array of its own so that the
     // compiler's wait for a slot's loads does not also wait for the other's.
     __shared__ __attribute__((aligned(1024))) uint8_t k_s0[kWaves][Gm::slot_bytes];
     __shared__ __attribute__((aligned(1024))) uint8_t v_s0[kWaves][Gm::slot_bytes];
     __shared__ __attribute__((aligned(1024))) uint8_t k_s1[kWaves][Gm::slot_bytes];
     __shared__ __attribute__((aligned(1024))) uint8_t v_s1[kWaves][Gm::slot_bytes];
+    // fp8 caches: each wave's V block converted to bf16 (one block).
+    constexpr int kCv = EB == 1 ? Geom<D, 2>::slot_bytes : 16;
+    __shared__ __attribute__((aligned(1024))) uint8_t v_cv[kWaves][kCv];
 
     const int lane = threadIdx.x & 63;
     const int wave = (int)uniform_u32(threadIdx.x >> 6);
@@ -250,7 +297,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
                 valid = min(kBS, t_end - tok0);
             }
         }
-        issue_block<D>(a.k_cache, a.v_cache, phys, blk_bytes, valid, voff, lane, ks, vs);
+        issue_block<Gm>(a.k_cache, a.v_cache, phys, blk_bytes, valid, voff, lane, ks, vs);
     };
     auto valid_rows = [&](int j) __attribute__((always_inline)) {
         return min(kBS, t_end - (blk0 + wave + kWaves * j) * kBS);
@@ -263,14 +310,21 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
 
     // Every path through the loop issues the same loads in the same order,
     // so the wait before each slot's reads is exact.
+    auto run = [&](const uint8_t *ks, const uint8_t *vs, int j) __attribute__((always_inline)) {
+        const uint8_t *vb = vs;
+        if constexpr (EB == 1) {
+            convert_v<D>(vs, v_cv[wave], lane);
+            __builtin_amdgcn_wave_barrier();
+            vb = v_cv[wave];
+        }
+        compute_block<D, EB>(ks, vb, valid_rows(j), causal_blk(j), tok0_of(j), lim, a.scale_log2, l16, g, w);
+    };
     issue(0, k_s0[wave], v_s0[wave]);
     issue(1, k_s1[wave], v_s1[wave]);
     for (int j = 0; j < nmine; j += 2) {
-        compute_block<D>(k_s0[wave], v_s0[wave], valid_rows(j), causal_blk(j), tok0_of(j), lim, a.scale_log2, l16, g, w);
+        run(k_s0[wave], v_s0[wave], j);
         issue(j + 2, k_s0[wave], v_s0[wave]);
-        if (j + 1 < nmine)
-            compute_block<D>(k_s1[wave], v_s1[wave], valid_rows(j + 1), causal_blk(j + 1), tok0_of(j + 1), lim,
-                             a.scale_log2, l16, g, w);
+        if (j + 1 < nmine) run(k_s1[wave], v_s1[wave], j + 1);
         issue(j + 3, k_s1[wave], v_s1[wave]);
     }
 
@@ -283,8 +337,16 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     // nothing but still write zeros) and passed the barrier.
     __builtin_amdgcn_s_waitcnt(0);
     const bool any_bad = __syncthreads_or(bad);
-    float *mo = reinterpret_cast<float *>(wave < 2 ? &k_s0[0][0] : &v_s0[0][0]) + (wave & 1) * 16 * D;
-    float *ml = reinterpret_cast<float *>(&k_s1[0][0]);      // [wave][16] m, then [wave][16] l
+    // Wave w's partial O (16 columns x D fp32): bf16 caches put two waves in
+    // each of k_s0 / v_s0, fp8 caches one wave in each of the four slots.
+    auto merge_area = [&](int v) __attribute__((always_inline)) -> float * {
+        if constexpr (EB == 2)
+            return reinterpret_cast<float *>(v < 2 ? &k_s0[0][0] : &v_s0[0][0]) + (v & 1) * 16 * D;
+        else
+            return reinterpret_cast<float *>(v == 0 ? &k_s0[0][0] : v == 1 ? &v_s0[0][0] : v == 2 ? &k_s1[0][0] : &v_s1[0][0]);
+    };
+    float *mo = merge_area(wave);
+    float *ml = reinterpret_cast<float *>(EB == 2 ? &k_s1[0][0] : &v_cv[0][0]);   // [wave][16] m, then l
     if (g == 0) {
         ml[wave * 16 + l16] = w.m;
         ml[kWaves * 16 + wave * 16 + l16] = w.l;
@@ -306,13 +368,13 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
                 const float mv = ml[v * 16 + head];
                 if (mv == kNegInf) continue;
                 const float sc = exp2_fast(mv - M);
-                const float *src = reinterpret_cast<const float *>(v < 2 ? &k_s0[0][0] : &v_s0[0][0]) + (v & 1) * 16 * D;
+                const float *src = merge_area(v);
                 L += ml[kWaves * 16 + v * 16 + head] * sc;
                 O += src[head * D + d] * sc;
             }
         }
         const size_t row = (((size_t)b * T + head / G) * a.Hq + hk * G + head % G) * a.splits + split;
-        float o_out = L > 0.f ? O / L : 0.f;
+        float o_out = L > 0.f ? O / L * a.v_scale : 0.f;
         float lse_out = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
         if (any_bad) {
             o_out = __builtin_nanf("");
@@ -406,12 +468,12 @@ __global__ void __launch_bounds__(kThreads) decode_combine_kernel(DecodeArgs a)
     }
 }
 
-template <int D>
+template <int D, int EB>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
 {
     const long long g1 = (long long)a.B * a.Hkv * a.splits;
     if (g1 <= 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)g1), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, EB>), dim3((unsigned)g1), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.B * a.T * a.Hq)), dim3(kThreads), 0, s, a);
@@ -420,10 +482,10 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs &a, int head_dim, hipStream_t s)
+hipError_t launch_decode(const DecodeArgs &a, int head_dim, bool kv_fp8, hipStream_t s)
 {
-    if (head_dim == 128) return launch_d<128>(a, s);
-    if (head_dim == 64) return launch_d<64>(a, s);
+    if (head_dim == 128) return kv_fp8 ? launch_d<128, 1>(a, s) : launch_d<128, 2>(a, s);
+    if (head_dim == 64) return kv_fp8 ? launch_d<64, 1>(a, s) : launch_d<64, 2>(a, s);
     return hipErrorInvalidValue;
 }
 

@@ -22,8 +22,8 @@ struct PrefillArgs {
 
 struct DecodeArgs {
     const uint16_t *q;            // [B,T,Hq,D] bf16 (T new tokens per sequence)
-    const uint16_t *k_cache;      // [num_blocks,16,Hkv,D] bf16
-    const uint16_t *v_cache;
+    const void *k_cache;          // [num_blocks,16,Hkv,D] bf16 or fp8 e4m3
+    const void *v_cache;
     const int32_t *block_table;   // [B,max_blocks]
     const int32_t *ctx_lens;      // [B]
     float *part_o;                // [B,T,Hq,splits,D] fp32
@@ -31,12 +31,13 @@ struct DecodeArgs {
     uint16_t *o;                  // [B,T,Hq,D] bf16
     float *lse;                   // [B,Hq,T] or nullptr
     int B, T, Hq, Hkv, num_blocks, max_blocks, splits;
-    float scale_log2;
+    float scale_log2;             // softmax scale (times the K dequantisation scale) times log2(e)
+    float v_scale;                // V dequantisation scale (1 for bf16 caches)
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_prefill_paged_bf16(const PrefillArgs &a, int head_dim, bool causal, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int head_dim, bool kv_fp8, hipStream_t s);
 
 }  // namespace attn

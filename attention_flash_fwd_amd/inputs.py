@@ -164,6 +164,9 @@ class DecodeInputs:
     device: str
     block_size: int = BLOCK_SIZE
     ctx: list = field(default_factory=list)
+    kv_format: str = "bf16"    # "bf16", or "fp8": uint8 e4m3 codes of value / scale
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def batch(self):
@@ -183,9 +186,24 @@ class DecodeInputs:
         dev = self.device if device is None else device
         n = self.ctx[b]
         shape = (n, self.n_kv_heads, self.head_dim)
-        k = _normal(shape, self.seed, "k", b + 1, self.device, torch.bfloat16)
-        v = _normal(shape, self.seed, "v", b + 1, self.device, torch.bfloat16)
+        k = _kv_values(shape, self.seed, "k", b + 1, self.device, self.kv_format, self.k_scale)
+        v = _kv_values(shape, self.seed, "v", b + 1, self.device, self.kv_format, self.v_scale)
         return k.to(dev), v.to(dev)
+
+
+E4M3_NAN_CODE = 0x7F          # an e4m3 NaN: fills unused fp8 cache slots
+
+
+def _kv_values(shape, seed, tag, index, device, kv_format, kv_scale):
+    """Cached K or V values: bf16, or the e4m3 codes (uint8) of value / scale
+    with torch's float8_e4m3fn conversion (N(0, 1) / scale stays far below
+    the e4m3 maximum of 448 for the scales used here)."""
+    if kv_format == "bf16":
+        return _normal(shape, seed, tag, index, device, torch.bfloat16)
+    if kv_format != "fp8":
+        raise ValueError(kv_format)
+    x = _normal(shape, seed, tag, index, device, torch.float32)
+    return (x / kv_scale).to(torch.float8_e4m3fn).view(torch.uint8)
 
 
 def decode_context_lengths(batch, ctx_min, ctx_max, seed):
@@ -197,7 +215,8 @@ def decode_context_lengths(batch, ctx_min, ctx_max, seed):
 
 
 def decode_inputs(ctx, n_q_heads, n_kv_heads, head_dim, seed=0, device="cpu",
-                  spare_blocks=0, block_size=BLOCK_SIZE, table_pad=0):
+                  spare_blocks=0, block_size=BLOCK_SIZE, table_pad=0, kv_format="bf16",
+                  k_scale=1.0, v_scale=1.0):
     """Paged decode inputs for per-sequence context lengths ``ctx``.
 
     The pool holds exactly the blocks the sequences need plus ``spare_blocks``
@@ -220,9 +239,13 @@ def decode_inputs(ctx, n_q_heads, n_kv_heads, head_dim, seed=0, device="cpu",
 
     dev = torch.device(device)
     q = _normal((B, n_q_heads, head_dim), seed, "q", 0, device, torch.bfloat16)
-    k_cache = torch.full((max(total, 1), block_size, n_kv_heads, head_dim), float("nan"),
-                         dtype=torch.bfloat16, device=dev)
-    v_cache = torch.full_like(k_cache, float("nan"))
+    pool_shape = (max(total, 1), block_size, n_kv_heads, head_dim)
+    if kv_format == "fp8":
+        k_cache = torch.full(pool_shape, E4M3_NAN_CODE, dtype=torch.uint8, device=dev)
+        v_cache = torch.full_like(k_cache, E4M3_NAN_CODE)
+    else:
+        k_cache = torch.full(pool_shape, float("nan"), dtype=torch.bfloat16, device=dev)
+        v_cache = torch.full_like(k_cache, float("nan"))
     kf = k_cache.view(-1, n_kv_heads, head_dim)
     vf = v_cache.view(-1, n_kv_heads, head_dim)
     tbl_dev = torch.from_numpy(table).to(dev)
@@ -230,8 +253,8 @@ def decode_inputs(ctx, n_q_heads, n_kv_heads, head_dim, seed=0, device="cpu",
         if ctx[b] == 0:
             continue
         shape = (ctx[b], n_kv_heads, head_dim)
-        kb = _normal(shape, seed, "k", b + 1, device, torch.bfloat16)
-        vb = _normal(shape, seed, "v", b + 1, device, torch.bfloat16)
+        kb = _kv_values(shape, seed, "k", b + 1, device, kv_format, k_scale)
+        vb = _kv_values(shape, seed, "v", b + 1, device, kv_format, v_scale)
         t = torch.arange(ctx[b], device=dev)
         slots = tbl_dev[b, t // block_size].long() * block_size + (t % block_size)
         kf[slots] = kb
@@ -239,7 +262,8 @@ def decode_inputs(ctx, n_q_heads, n_kv_heads, head_dim, seed=0, device="cpu",
         del kb, vb, t, slots
     inp = DecodeInputs(q=q, k_cache=k_cache, v_cache=v_cache, block_table=tbl_dev,
                        ctx_lens=torch.tensor(ctx, dtype=torch.int32, device=dev),
-                       seed=int(seed), device=str(dev), block_size=block_size, ctx=ctx)
+                       seed=int(seed), device=str(dev), block_size=block_size, ctx=ctx,
+                       kv_format=kv_format, k_scale=float(k_scale), v_scale=float(v_scale))
     return inp
 
 

@@ -248,6 +248,37 @@ attn_status_t attn_decode_paged_multi(const void *q, const void *k_cache, const 
                                       attn_stream_t stream);
 
 /*
+ * attn_decode_paged_fp8 -- attn_decode_paged_multi over an 8-bit KV cache:
+ * half the bytes per cached token, for decode steps limited by the bandwidth
+ * of reading the cache ("5.2 推理加速的未来趋势", co-design layer: low-precision
+ * KV caches as a lever on memory traffic; "推理加速" interview notes,
+ * techniques table: KV-cache quantisation).  The pages fix no format; this
+ * library reads OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, subnormals, 0x7F / 0xFF = NaN, no infinities, largest
+ * finite value 448) with one scale per tensor:
+ *     K = e4m3(k_cache) * k_scale,   V = e4m3(v_cache) * v_scale.
+ *
+ *   k_cache, v_cache  [num_blocks, block_size, n_kv_heads, head_dim] uint8
+ *                     e4m3 codes
+ *   k_scale, v_scale  finite dequantisation scales (ATTN_ERR_SHAPE otherwise)
+ *   everything else as for attn_decode_paged_multi, including the workspace
+ *   (attn_decode_multi_workspace_bytes).
+ *
+ * The codes are widened exactly to bf16 for the matrix-core products;
+ * k_scale is folded into the score scale and v_scale applied to the fp32
+ * partial outputs.
+ */
+attn_status_t attn_decode_paged_fp8(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_table, const int32_t *ctx_lens,
+                                    void *o, float *lse,
+                                    int batch, int seqlen_q, int n_q_heads, int n_kv_heads,
+                                    int head_dim, int num_blocks, int block_size,
+                                    int max_blocks_per_seq, int num_splits, float scale,
+                                    float k_scale, float v_scale,
+                                    void *workspace, size_t workspace_bytes,
+                                    attn_stream_t stream);
+
+/*
  * attn_decode_multi_workspace_bytes -- workspace of attn_decode_paged_multi:
  * partial outputs [batch, seqlen_q, n_q_heads, splits, head_dim] fp32, then
  * their log-sum-exps [batch, seqlen_q, n_q_heads, splits] fp32.  Returns 0
@@ -263,7 +294,7 @@ const char *attn_status_string(attn_status_t status);
 /* ABI version of this header: (major << 16) | minor. */
 int attn_abi_version(void);
 
-#define ATTN_ABI_VERSION ((1 << 16) | 2)
+#define ATTN_ABI_VERSION ((1 << 16) | 3)
 
 #ifdef __cplusplus
 }

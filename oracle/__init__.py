@@ -178,3 +178,31 @@ def lse_combine(o_parts, lse_parts):
     rc = lib.oracle_lse_combine(_ptr(op), _ptr(lp), n, D, _ptr(o), _ptr(lse))
     _check(rc, "oracle_lse_combine")
     return o, float(lse[0])
+
+
+def e4m3_decode(codes):
+    """OCP FP8 E4M3 codes (uint8) -> exact float64 values, written from the
+    format's definition: sign bit, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent 0 encodes subnormals (m / 8) * 2^-6; exponent 15 with
+    mantissa 7 is NaN; there are no infinities.  (The pages fix no 8-bit
+    format; this is the reading the library documents for its FP8 KV cache,
+    "5.2 推理加速的未来趋势" co-design layer on low-precision KV caches.)"""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    val = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    val = sign * val
+    return np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+
+
+def decode_fp8(q, k_codes, v_codes, scale: float, k_scale: float, v_scale: float, nthreads: int = 0):
+    """Decode over an e4m3 KV cache with per-tensor scales:
+    K = e4m3(k) * k_scale, V = e4m3(v) * v_scale.  The codes decode exactly
+    to fp32, k_scale joins the score scale (scale * q . (k * k_scale) =
+    (scale * k_scale) * q . k) and v_scale multiplies the output (O is linear
+    in V), so no value is rounded before the fp64 arithmetic of `decode`."""
+    ks = [e4m3_decode(k).astype(np.float32) for k in k_codes]
+    vs = [e4m3_decode(v).astype(np.float32) for v in v_codes]
+    o, lse = decode(q, ks, vs, float(scale) * float(k_scale), nthreads)
+    return o * float(v_scale), lse

@@ -59,7 +59,7 @@ def test_exports_are_c_symbols():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.attn_abi_version() == (1 << 16) | 2
+    assert lib.attn_abi_version() == (1 << 16) | 3
     for code in range(8):
         s = lib.attn_status_string(code).decode()
         assert s and s != "unknown status"
@@ -177,6 +177,23 @@ def test_decode_multi_validation(lib):
     assert lib.attn_decode_multi_workspace_bytes(2, 1, 8, 2, 128, 5, 16, 4) == \
         lib.attn_decode_workspace_bytes(2, 8, 2, 128, 5, 16, 4)
     assert lib.attn_decode_multi_workspace_bytes(2, 0, 8, 2, 128, 5, 16, 4) == 0
+
+
+def decode_fp8(lib, ks=0.05, vs=0.05, T=1, q=FAKE, ws=FAKE, B=2, Hq=8, Hkv=2, D=128, max_blocks=5, splits=4):
+    P = ctypes.c_void_p
+    ws_bytes = lib.attn_decode_multi_workspace_bytes(B, T, Hq, Hkv, D, max_blocks, 16, splits)
+    return lib.attn_decode_paged_fp8(P(q), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), B, T, Hq,
+                                     Hkv, D, 10, 16, max_blocks, splits, 0.1, ks, vs, P(ws), ws_bytes, P(0))
+
+
+def test_decode_fp8_validation(lib):
+    assert decode_fp8(lib, ks=float("nan")) == SHAPE
+    assert decode_fp8(lib, vs=float("inf")) == SHAPE
+    assert decode_fp8(lib, D=96) == UNSUP
+    assert decode_fp8(lib, T=5) == UNSUP
+    assert decode_fp8(lib, q=FAKE_MIS) == ALIGN
+    assert decode_fp8(lib, ws=0) == WORKSPACE
+    assert decode_fp8(lib, B=0, q=0) == OK
 
 
 def test_workspace_and_split_rules(lib):

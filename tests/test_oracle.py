@@ -340,3 +340,56 @@ def test_decode_zero_context():
     o, lse = oracle.decode(q, ks, vs, 0.5)
     assert np.all(o[0] == 0) and np.all(lse[0] == -np.inf)
     assert np.all(np.isfinite(lse[1]))
+
+
+# ------------------------------------------------------------ fp8 (e4m3) ---
+def test_e4m3_decode_matches_library_conversion():
+    # All 256 codes against torch's float8_e4m3fn -> float32 conversion.
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = oracle.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_e4m3_decode_hand_values():
+    vals = {0x38: 1.0, 0xB8: -1.0, 0x3C: 1.5, 0x7E: 448.0, 0xFE: -448.0, 0x01: 2.0 ** -9,
+            0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x00: 0.0, 0x40: 2.0, 0x30: 0.5, 0x28: 0.25}
+    got = oracle.e4m3_decode(np.array(list(vals), np.uint8))
+    assert list(got) == list(vals.values())
+    assert np.isnan(oracle.e4m3_decode(np.array([0x7F, 0xFF], np.uint8))).all()
+    assert np.signbit(oracle.e4m3_decode(np.array([0x80], np.uint8))[0])
+
+
+def _fp8_case(seed, ctx=(37, 5), Hq=4, Hkv=2, D=8):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((len(ctx), Hq, D)).astype(np.float32)
+    # finite codes only (exclude the NaN codes 0x7F / 0xFF)
+    kc = [rng.integers(0, 0x7F, size=(c, Hkv, D), dtype=np.uint8) | (rng.integers(0, 2, size=(c, Hkv, D), dtype=np.uint8) << 7)
+          for c in ctx]
+    vc = [rng.integers(0, 0x7F, size=(c, Hkv, D), dtype=np.uint8) for c in ctx]
+    return q, kc, vc
+
+
+def test_decode_fp8_equals_decode_of_dequantised_cache():
+    # With power-of-two scales, code * scale is exact in fp32, so dequantising
+    # first and running the plain decode must give the same numbers.
+    q, kc, vc = _fp8_case(1)
+    ks, vs, scale = 2.0 ** -5, 2.0 ** -3, 0.3
+    o, l = oracle.decode_fp8(q, kc, vc, scale, ks, vs)
+    kd = [(oracle.e4m3_decode(k) * ks).astype(np.float32) for k in kc]
+    vd = [(oracle.e4m3_decode(v) * vs).astype(np.float32) for v in vc]
+    o2, l2 = oracle.decode(q, kd, vd, scale)
+    assert np.allclose(o, o2, rtol=1e-12, atol=1e-14) and np.allclose(l, l2, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_fp8_scale_roles():
+    q, kc, vc = _fp8_case(2)
+    o, l = oracle.decode_fp8(q, kc, vc, 0.25, 0.5, 1.0)
+    o2, l2 = oracle.decode_fp8(q, kc, vc, 0.5, 0.25, 3.0)     # same score scale, V scaled by 3
+    assert np.allclose(o2, 3.0 * o, rtol=1e-12) and np.allclose(l2, l, rtol=1e-12)
+    o3, _ = oracle.decode_fp8(q, kc, vc, 0.25, 1.0, 1.0)      # different score scale
+    assert not np.allclose(o3, o)

@@ -465,3 +465,71 @@ def test_decode_multi_single_token_is_decode(afa):
                                     inp.block_table, inp.ctx_lens, num_splits=8)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2[:, 0]) and torch.equal(l1, l2[:, :, 0])
+
+
+# ------------------------------------------------------ fp8 (e4m3) KV decode ---
+def fp8_oracle(inp, q, scale, seqs=None):
+    """Oracle on the cache's e4m3 codes: q [B,Hq,D] (one token) or [B,T,Hq,D]."""
+    seqs = list(range(len(inp.ctx))) if seqs is None else seqs
+    kv = [inp.logical_kv(b, device="cpu") for b in seqs]
+    qn = to_np(q)
+    if q.dim() == 3:
+        return oracle.decode_fp8(qn[seqs], [x[0].numpy() for x in kv], [x[1].numpy() for x in kv],
+                                 scale, inp.k_scale, inp.v_scale)
+    os_, ls_ = [], []
+    for i, b in enumerate(seqs):
+        k = oracle.e4m3_decode(kv[i][0].numpy()).astype(np.float32)[None]
+        v = oracle.e4m3_decode(kv[i][1].numpy()).astype(np.float32)[None]
+        o, l = oracle.attention(qn[b:b + 1], k, v, True, scale * inp.k_scale)
+        os_.append(o[0] * inp.v_scale)
+        ls_.append(l[0])
+    return np.stack(os_), np.stack(ls_)
+
+
+@pytest.mark.parametrize("ctx,T,Hq,Hkv,D,splits,ks,vs", [
+    ([1, 15, 16, 17, 513], 1, 8, 2, 128, 4, 2.0 ** -5, 2.0 ** -5),
+    ([100, 2000], 1, 32, 8, 128, 16, 0.0371, 0.0219),      # scales that are not powers of two
+    ([257, 1500, 31], 1, 64, 8, 128, 8, 0.03, 0.05),       # G = 8
+    ([300, 45], 1, 8, 2, 64, 3, 0.04, 0.04),                # D = 64
+    ([300, 77, 1000], 4, 8, 2, 128, 4, 0.03, 0.03),        # 4 new tokens per sequence
+])
+def test_decode_fp8_matches_oracle(afa, ctx, T, Hq, Hkv, D, splits, ks, vs):
+    from attention_flash_fwd_amd import inputs
+    say(f"case decode_fp8 ctx{ctx} T{T} Hq{Hq} Hkv{Hkv} D{D} splits{splits} ks{ks} vs{vs}")
+    inp = inputs.decode_inputs(ctx, Hq, Hkv, D, seed=len(ctx) * 7 + Hq + T, device="cuda", spare_blocks=2,
+                               kv_format="fp8", k_scale=ks, v_scale=vs)
+    q = inp.q if T == 1 else inputs.chunk_queries(len(ctx), T, Hq, D, seed=5, device="cuda")
+    scale = 1 / math.sqrt(D)
+    o, lse = afa.decode_paged_fp8(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens, ks, vs,
+                                  num_splits=splits, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = fp8_oracle(inp, q, scale)
+    check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse), l_ref, BF16_LSE_ABS)
+
+
+def test_decode_fp8_permutation_and_nan_contract(afa):
+    from attention_flash_fwd_amd import inputs
+    say("case decode_fp8 block permutation / bad block id")
+    inp = inputs.decode_inputs([1000, 37, 4097], 32, 8, 128, seed=6, device="cuda", kv_format="fp8",
+                               k_scale=0.03, v_scale=0.04)
+    o_a, l_a = afa.decode_paged_fp8(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                    0.03, 0.04, num_splits=16)
+    nb = inp.k_cache.shape[0]
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(3)).cuda()
+    k2 = torch.empty_like(inp.k_cache)
+    v2 = torch.empty_like(inp.v_cache)
+    k2[perm] = inp.k_cache
+    v2[perm] = inp.v_cache
+    tbl = inp.block_table.long()
+    tbl2 = torch.where(tbl >= 0, perm[tbl.clamp(min=0)], tbl).to(torch.int32).contiguous()
+    o_b, l_b = afa.decode_paged_fp8(inp.q, k2, v2, tbl2, inp.ctx_lens, 0.03, 0.04, num_splits=16)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b)
+    tbl3 = inp.block_table.clone()
+    tbl3[1, 0] = -3
+    o_c, l_c = afa.decode_paged_fp8(inp.q, inp.k_cache, inp.v_cache, tbl3, inp.ctx_lens, 0.03, 0.04,
+                                    num_splits=16)
+    torch.cuda.synchronize()
+    assert torch.isnan(o_c[1]).all() and torch.isnan(l_c[1]).all()
+    assert torch.equal(o_c[0], o_a[0]) and torch.equal(o_c[2], o_a[2])
