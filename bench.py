@@ -33,7 +33,8 @@ PEAK_HBM_BPS = 8.0e12         # MI355X HBM3E
 COPY_BYTES = 1 << 30          # calibration copy (profiling runs only)
 # Workloads beyond the hot path's step, timed on their own after it (never
 # part of `value` or `ms_per_step`).
-EXTRAS = ("chunked_prefill", "decode_multi")
+EXTRAS = ("chunked_prefill", "decode_multi", "decode_b64_fp8")
+FP8_SCALE = 1.0 / 32          # per-tensor K and V scale of the fp8 extra
 MULTI_T = 4                   # new tokens per sequence in the multi-token decode extra
 METRIC = "prefill attn TFLOP/s + decode KV GB/s, % of MI355X bf16/HBM peak"
 
@@ -196,6 +197,15 @@ def main():
         mo = torch.empty_like(mq)
         mlse = torch.empty((mcfg.batch, mcfg.n_q_heads, MULTI_T), dtype=torch.float32, device=dev)
         extra_in["decode_multi"] = (mcfg, minp, mq, mws, mo, mlse)
+    if "decode_b64_fp8" in parts:
+        fcfg = inputs.DECODE_B64
+        fctx = inputs.decode_context_lengths(fcfg.batch, fcfg.ctx_min, fcfg.ctx_max, fcfg.seed)
+        finp = inputs.decode_inputs(fctx, fcfg.n_q_heads, fcfg.n_kv_heads, fcfg.head_dim, fcfg.seed, dev,
+                                    kv_format="fp8", k_scale=FP8_SCALE, v_scale=FP8_SCALE)
+        fws = afa.decode_workspace(finp.q, finp.k_cache, finp.block_table, fcfg.num_splits)
+        fo = torch.empty_like(finp.q)
+        flse = torch.empty(finp.q.shape[:2], dtype=torch.float32, device=dev)
+        extra_in["decode_b64_fp8"] = (fcfg, finp, fws, fo, flse)
     if pf_in is not None:
         q, k, v = pf_in
         pf_o = torch.empty_like(q)
@@ -231,7 +241,15 @@ def main():
                                num_splits=mcfg.num_splits, scale=mcfg.scale, out=mo, lse_out=mlse,
                                workspace=mws)
 
+    def run_fp8():
+        fcfg, finp, fws, fo, flse = extra_in["decode_b64_fp8"]
+        afa.decode_paged_fp8(finp.q, finp.k_cache, finp.v_cache, finp.block_table, finp.ctx_lens,
+                             FP8_SCALE, FP8_SCALE, num_splits=fcfg.num_splits, scale=fcfg.scale, out=fo,
+                             lse_out=flse, workspace=fws)
+
     extra_runners = []
+    if "decode_b64_fp8" in extra_in:
+        extra_runners.append(("decode_b64_fp8", run_fp8))
     if "chunked_prefill" in extra_in:
         extra_runners.append(("chunked_prefill", run_chunked))
     if "decode_multi" in extra_in:
@@ -282,6 +300,16 @@ def main():
             tf = cp.flops() / (ms * 1e-3) / 1e12
             extras[name] = {"workload": cp.name, "ms": ms, "tflops": tf,
                             "frac_of_peak": tf * 1e12 / PEAK_BF16_FLOPS, "flops": cp.flops()}
+        elif name == "decode_b64_fp8":
+            fcfg, finp = extra_in[name][:2]
+            B, Hq, D = finp.q.shape
+            used_blocks = sum((c + 15) // 16 for c in finp.ctx)
+            nb = (inputs.decode_kv_bytes(finp.ctx, finp.n_kv_heads, D, elem_bytes=1) + 2 * B * Hq * D * 2
+                  + used_blocks * 4 + B * 4)
+            gbps = nb / (ms * 1e-3) / 1e9
+            extras[name] = {"workload": fcfg.name.replace("bf16", "fp8kv"), "ms": ms, "gbps": gbps,
+                            "frac_of_peak": gbps * 1e9 / PEAK_HBM_BPS, "bytes": nb,
+                            "num_splits": fcfg.num_splits, "kv_format": "e4m3, per-tensor scale"}
         elif name == "decode_multi":
             mcfg, minp, mq = extra_in[name][:3]
             nb = decode_bytes(minp, mcfg.n_q_heads) + 2 * (MULTI_T - 1) * mq[:, 0].numel() * 2
