@@ -157,8 +157,10 @@ attn_status_t attn_prefill_paged(const void *q, const void *k_cache, const void 
  * attn_decode_paged will use for these arguments.  num_splits >= 1 is
  * returned unchanged (after the range check of attn_decode_paged);
  * num_splits <= 0 asks for the library's choice, which depends only on the
- * arguments given here (never on device data): enough chunks to occupy the
- * GPU, none shorter than 256 tokens.  Returns 0 for invalid arguments.
+ * arguments given here (never on device data): chunks of about 2048 tokens
+ * of the longest sequence the table can hold, or more chunks (none shorter
+ * than 256 tokens) when that is needed for about 2048 workgroups to occupy
+ * the GPU.  Returns 0 for invalid arguments.
  */
 int attn_decode_num_splits(int batch, int n_kv_heads, int max_blocks_per_seq,
                            int block_size, int num_splits);
