@@ -76,18 +76,21 @@ KERNEL_SOURCES = {
     "decode": ["attention_flash_fwd_amd/csrc/decode.hip", "attention_flash_fwd_amd/csrc/gfx950.hpp",
                "attention_flash_fwd_amd/csrc/kernels.hpp"],
 }
-TRAFFIC_KEYS = {"prefill": "prefill_8k", "decode_b64": "decode_b64", "decode_128k": "decode_128k"}
+def sources_of(part):
+    return KERNEL_SOURCES["prefill" if "prefill" in part else "decode"]
 
 
-def load_traffic(part, kernel_digest):
+def load_traffic(part, kernel_digest=None):
     """HBM bytes (read + write) per call of `part` from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE runs, if they were taken on the current
     kernel source; else None."""
+    if kernel_digest is None:
+        kernel_digest = source_digest(sources_of(part))
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f).get(TRAFFIC_KEYS[part])
+        rec = json.load(f).get(part)
     if rec is None or rec.get("source_digest") != kernel_digest:
         return None
     return rec.get("hbm_bytes")
@@ -350,7 +353,7 @@ def main():
     decode_roofline = {
         name: {"bound": "hbm", "achieved": p["gbps"], "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                "frac": p["frac_of_peak"], "per_launch_bytes": p["bytes"], "avg_launch_ms": p["ms"],
-               "traffic": load_traffic(name, source_digest(KERNEL_SOURCES["decode"])),
+               "traffic": load_traffic(name),
                "note": "split + combine kernels of one attn_decode_paged call"}
         for name, p in out_parts.items() if name.startswith("decode")}
 
@@ -360,6 +363,8 @@ def main():
                      for name, (cfg, inp, ws, o, lse) in dec.items()}
         cpu = cpu_baseline(parts, pf_cfg, pf_in, dec_parts)
 
+    for name, rec in extras.items():
+        rec["traffic"] = load_traffic(name)
     workload = " + ".join(out_parts[p]["workload"] for p in out_parts if p != "copy")
     rec = {
         "metric": METRIC,
