@@ -17,6 +17,7 @@ namespace {
 
 constexpr long long kMaxElems = 1LL << 31;   // per-tensor element limit of the prefill path
 constexpr int kBlockSize = 16;
+constexpr int kMaxColumns = 256;     // (query heads per KV head) x (new tokens) in paged decode
 constexpr float kLog2e = 1.44269504088896340736f;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -202,7 +203,7 @@ attn_status_t decode_common(const void *q, const void *k_cache, const void *v_ca
     if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_SHAPE;
     if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
     if (block_size != kBlockSize) return ATTN_ERR_UNSUPPORTED;
-    if ((long long)(n_q_heads / n_kv_heads) * seqlen_q > 16) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)(n_q_heads / n_kv_heads) * seqlen_q > kMaxColumns) return ATTN_ERR_UNSUPPORTED;
     if (num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_UNSUPPORTED;
     if (kv_fp8 && !(std::isfinite(k_scale) && std::isfinite(v_scale))) return ATTN_ERR_SHAPE;
     if ((long long)max_blocks_per_seq * block_size >= kMaxElems) return ATTN_ERR_SHAPE;

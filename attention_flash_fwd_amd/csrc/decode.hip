@@ -19,7 +19,8 @@
 //     P = 2^(S - m), lazy rescale of (l, O) when the max grows by > 2^8
 //     O^T (D x 16 columns)       += V^T P^T  D/16 x 16x16x16 bf16 MFMA
 //   New token t sees the keys up to position ctx - T + t; that limit is only
-//   checked on the blocks that reach past ctx - T.
+//   checked on the blocks that reach past ctx - T.  More than 16 columns are
+//   split over column tiles, one workgroup each.
 //   The score accumulator of a lane (4 tokens of one head) is exactly the
 //   B operand the 16x16x16 product wants, and the V^T operand comes from one
 //   transposing LDS read per 16 rows of d.  Cache slots past the chunk end
@@ -218,12 +219,23 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     const int wave = (int)uniform_u32(threadIdx.x >> 6);
     const int l16 = lane & 15, g = lane >> 4;
 
-    const int split = blockIdx.x % a.splits;
-    const int hk = (blockIdx.x / a.splits) % a.Hkv;
-    const int b = blockIdx.x / (a.splits * a.Hkv);
     const int G = a.Hq / a.Hkv;
     const int T = a.T;                  // new tokens per sequence
     const int GT = G * T;               // matrix-core columns in use: (token, head) pairs
+    // Workgroup -> (column tile, chunk, KV head, sequence).  More than 16
+    // columns take several column tiles; the tiles of one (chunk, KV head,
+    // sequence) get ids 8 apart, so they run on the same XCD (ids go
+    // round-robin over the 8 XCDs) and share its L2 copy of the K/V blocks.
+    const int n_ct = (GT + 15) / 16;
+    const int L = blockIdx.x, r8 = L >> 3;
+    const int ct = r8 % n_ct;
+    const int unit = (r8 / n_ct) * 8 + (L & 7);
+    if (unit >= a.B * a.Hkv * a.splits) return;     // padding of the id space (uniform)
+    const int split = unit % a.splits;
+    const int hk = (unit / a.splits) % a.Hkv;
+    const int b = unit / (a.splits * a.Hkv);
+    const int col0 = 16 * ct;
+    const int NC = min(16, GT - col0);  // columns of this tile
 
     // Sequence length through the scalar cache: everything derived from it
     // (chunk bounds, trip counts) stays wave-uniform.
@@ -246,8 +258,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
         // Column col = t G + g holds query head hk G + g of new token t.
         // Columns past G T read the last valid one and are zeroed (no branch
         // around the load).
-        const bool hv = l16 < GT;
-        const int col = min(l16, GT - 1);
+        const bool hv = l16 < NC;
+        const int col = col0 + min(l16, NC - 1);
         const uint16_t *qp = a.q + (((size_t)b * T + col / G) * a.Hq + hk * G + col % G) * D + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
@@ -304,7 +316,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     };
     // New token t sees keys up to position ctx - T + t; only blocks reaching
     // past ctx - T need that check.
-    const int lim = ctx - T + (l16 < GT ? l16 / G : 0);
+    const int lim = ctx - T + (l16 < NC ? (col0 + l16) / G : 0);
     auto tok0_of = [&](int j) __attribute__((always_inline)) { return (blk0 + wave + kWaves * j) * kBS; };
     auto causal_blk = [&](int j) __attribute__((always_inline)) { return T > 1 && tok0_of(j) + kBS - 1 > ctx - T; };
 
@@ -356,8 +368,9 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
         *reinterpret_cast<f32x4_t *>(mo + l16 * D + 16 * db + 4 * g) = w.o[db];
     __syncthreads();
 
-    for (int idx = threadIdx.x; idx < GT * D; idx += kThreads) {
-        const int head = idx / D, d = idx % D;      // head = matrix-core column
+    for (int idx = threadIdx.x; idx < NC * D; idx += kThreads) {
+        const int head = idx / D, d = idx % D;      // head = matrix-core column of this tile
+        const int gcol = col0 + head;
         float M = kNegInf;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) M = fmaxf(M, ml[v * 16 + head]);
@@ -373,7 +386,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
                 O += src[head * D + d] * sc;
             }
         }
-        const size_t row = (((size_t)b * T + head / G) * a.Hq + hk * G + head % G) * a.splits + split;
+        const size_t row = (((size_t)b * T + gcol / G) * a.Hq + hk * G + gcol % G) * a.splits + split;
         float o_out = L > 0.f ? O / L * a.v_scale : 0.f;
         float lse_out = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
         if (any_bad) {
@@ -471,7 +484,9 @@ __global__ void __launch_bounds__(kThreads) decode_combine_kernel(DecodeArgs a)
 template <int D, int EB>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
 {
-    const long long g1 = (long long)a.B * a.Hkv * a.splits;
+    const long long units = (long long)a.B * a.Hkv * a.splits;
+    const long long n_ct = ((long long)(a.Hq / a.Hkv) * a.T + 15) / 16;
+    const long long g1 = (units + 7) / 8 * 8 * n_ct;
     if (g1 <= 0) return hipSuccess;
     hipLaunchKernelGGL((decode_split_kernel<D, EB>), dim3((unsigned)g1), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();

@@ -199,7 +199,7 @@ size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
  * beyond fp32 rounding.  Cache slots past ctx_lens[b] are never read, so
  * they may hold anything, NaN included.
  *
- * Supported: head_dim 64 or 128; block_size 16; n_q_heads / n_kv_heads <= 16;
+ * Supported: head_dim 64 or 128; block_size 16; n_q_heads / n_kv_heads <= 256;
  * num_splits in [1, ATTN_MAX_SPLITS] or <= 0 for the library's choice.
  * ctx_lens[b] == 0 gives O = 0, lse = -inf.
  * Device-side contract violations do not fault: a sequence whose ctx_lens
@@ -237,7 +237,7 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
  * and sees the keys at positions <= ctx_lens[b] - seqlen_q + t (causal among
  * the new tokens; the result equals attn_prefill_paged with the same
  * arguments).  A token with no visible key gets O = 0, lse = -inf.
- * Supported: (n_q_heads / n_kv_heads) * seqlen_q <= 16, plus the limits of
+ * Supported: (n_q_heads / n_kv_heads) * seqlen_q <= 256, plus the limits of
  * attn_decode_paged; seqlen_q == 1 is attn_decode_paged.
  */
 attn_status_t attn_decode_paged_multi(const void *q, const void *k_cache, const void *v_cache,

@@ -108,7 +108,7 @@ def decode(lib, q=FAKE, kc=FAKE, vc=FAKE, tbl=FAKE, ctx=FAKE, o=FAKE, lse=FAKE, 
 def test_decode_validation(lib):
     assert decode(lib, D=80) == UNSUP
     assert decode(lib, bs=32) == UNSUP
-    assert decode(lib, Hq=34, Hkv=2) == UNSUP        # 17 query heads per KV head
+    assert decode(lib, Hq=514, Hkv=2) == UNSUP       # 257 query heads per KV head (> 256 columns)
     assert decode(lib, splits=257) == UNSUP
     assert decode(lib, Hq=6, Hkv=4) == SHAPE
     assert decode(lib, B=-1) == SHAPE
@@ -166,8 +166,8 @@ def decode_multi(lib, T=2, q=FAKE, ws=FAKE, B=2, Hq=8, Hkv=2, D=128, max_blocks=
 
 def test_decode_multi_validation(lib):
     assert decode_multi(lib, T=0) == SHAPE
-    assert decode_multi(lib, T=5, Hq=8, Hkv=2) == UNSUP     # 4 heads x 5 tokens > 16 columns
-    assert decode_multi(lib, T=2, Hq=16, Hkv=1) == UNSUP
+    assert decode_multi(lib, T=65, Hq=8, Hkv=2) == UNSUP    # 4 heads x 65 tokens > 256 columns
+    assert decode_multi(lib, T=17, Hq=16, Hkv=1) == UNSUP
     assert decode_multi(lib, T=4, q=FAKE_MIS) == ALIGN
     assert decode_multi(lib, T=4, ws=0) == WORKSPACE
     need = lib.attn_decode_multi_workspace_bytes(2, 4, 8, 2, 128, 5, 16, 4)
@@ -190,7 +190,7 @@ def test_decode_fp8_validation(lib):
     assert decode_fp8(lib, ks=float("nan")) == SHAPE
     assert decode_fp8(lib, vs=float("inf")) == SHAPE
     assert decode_fp8(lib, D=96) == UNSUP
-    assert decode_fp8(lib, T=5) == UNSUP
+    assert decode_fp8(lib, T=65) == UNSUP
     assert decode_fp8(lib, q=FAKE_MIS) == ALIGN
     assert decode_fp8(lib, ws=0) == WORKSPACE
     assert decode_fp8(lib, B=0, q=0) == OK

@@ -436,6 +436,9 @@ def test_prefill_paged_long_chunk_sampled(afa):
     ([513, 2049], 2, 64, 8, 128, 16),           # the long-context head layout, T = 2
     ([129, 4000], 8, 16, 8, 128, 0),            # G = 2, T = 8, automatic splits
     ([390, 45], 4, 8, 2, 64, 5),                # D = 64
+    ([300, 1500], 4, 64, 8, 128, 8),            # G*T = 32: two column tiles
+    ([77, 2049, 600], 5, 64, 8, 128, 6),        # G*T = 40: a partial third tile
+    ([513, 31], 1, 64, 2, 128, 4),              # one token, G = 32
 ])
 def test_decode_multi_matches_oracle_and_chunked_prefill(afa, ctx, T, Hq, Hkv, D, splits):
     say(f"case decode_multi ctx{ctx} T{T} Hq{Hq} Hkv{Hkv} D{D} splits{splits}")
@@ -492,6 +495,7 @@ def fp8_oracle(inp, q, scale, seqs=None):
     ([257, 1500, 31], 1, 64, 8, 128, 8, 0.03, 0.05),       # G = 8
     ([300, 45], 1, 8, 2, 64, 3, 0.04, 0.04),                # D = 64
     ([300, 77, 1000], 4, 8, 2, 128, 4, 0.03, 0.03),        # 4 new tokens per sequence
+    ([700, 90], 4, 64, 8, 128, 8, 0.03, 0.05),             # G*T = 32: two column tiles
 ])
 def test_decode_fp8_matches_oracle(afa, ctx, T, Hq, Hkv, D, splits, ks, vs):
     from attention_flash_fwd_amd import inputs
