@@ -187,6 +187,46 @@ def test_prefill_invariants(afa):
     assert (l5 - cnt.log()[None, None, :]).abs().max().item() <= 1e-5
 
 
+@pytest.mark.parametrize("dtype,scale_mul,q_mul", [
+    ("bf16", -1.0, 1.0),        # negative scale: the kernel flips Q's sign bits
+    ("bf16", 1.0, 16.0),        # large logits: Q x 16 (exact in bf16)
+    ("f32", -1.0, 1.0),
+])
+def test_prefill_negative_scale_and_large_logits(afa, dtype, scale_mul, q_mul):
+    say(f"case prefill {dtype} scale x{scale_mul} q x{q_mul}")
+    B, S, Hq, Hkv, D = 1, 260, 4, 2, 128
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v = gen_prefill(B, S, S, Hq, Hkv, D, tdt, 31)
+    q = q * q_mul
+    scale = scale_mul / math.sqrt(D)
+    o, lse = run_prefill(afa, q, k, v, True, scale)
+    o_ref, lse_ref = oracle.attention(to_np(q), to_np(k), to_np(v), True, scale)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    if dtype == "bf16":
+        check_o(o, o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+        check_lse(lse, lse_ref, BF16_LSE_ABS)
+    else:
+        check_o(o, o_ref, F32_MAX_ABS)
+        check_lse(lse, lse_ref, F32_MAX_ABS)
+
+
+def test_decode_negative_scale_and_large_logits(afa):
+    say("case decode scale < 0 and q x 16")
+    inp = gen_decode([700, 33], 8, 2, 128, seed=41)
+    for scale, qm in ((-1 / math.sqrt(128), 1.0), (1 / math.sqrt(128), 16.0)):
+        q = (inp.q * qm).contiguous()
+        o, lse = afa.decode_paged(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                  num_splits=3, scale=scale)
+        torch.cuda.synchronize()
+        qn = to_np(q)
+        ref = [oracle.decode(qn[b:b + 1], [to_np(inp.logical_kv(b)[0])], [to_np(inp.logical_kv(b)[1])], scale)
+               for b in range(2)]
+        o_ref = np.concatenate([r[0] for r in ref])
+        l_ref = np.concatenate([r[1] for r in ref])
+        check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+        check_lse(to_np(lse), l_ref, BF16_LSE_ABS)
+
+
 # -------------------------------------------------------------- decode ---
 def gen_decode(ctx, Hq, Hkv, D, seed, device="cuda", spare_blocks=3, table_pad=2):
     from attention_flash_fwd_amd import inputs
