@@ -7,33 +7,44 @@
 // output; chenyy20.com "抱infra脚", Flash Attention 基本原理 / 核心技术:
 // tiling, online softmax, fusion of QK + softmax + PV; "GPU Kernel 调度：
 // 大模型推理的拐点 2026", FlashAttention evolution: query blocks in parallel,
-// K/V blocks pipelined, row-max / row-sum reductions):
+// K/V blocks pipelined, row-max / row-sum reductions; its note on the cost
+// of warp specialisation motivates the two wave groups below):
 //
-//   one workgroup = 128 query rows of one (batch, query head), 4 waves of 32
-//   rows each.  K/V tiles of 64 keys stream through a two-stage LDS ring fed
-//   by buffer loads that write LDS directly (no register staging; rows past
-//   the end of the sequence read as zero), so tile j+1 is in flight while
-//   tile j is computed.  Per tile and wave:
-//     S^T = K Q^T          32x32x16 bf16 MFMA; one lane = one query row, so
-//                          the row max is an in-lane reduction plus one
-//                          exchange between the two wave halves
-//     causal / ragged mask only on tiles that cross the diagonal or the end
-//     online softmax       exp2 domain: p = 2^(s * scale*log2e - m) is one
-//                          FMA + one v_exp_f32 per score.  Lazy rescaling:
-//                          the exponent reference m only moves when the row
-//                          max has grown by more than 2^8, so most tiles skip
-//                          rescaling O; the result is the same up to rounding
-//     P -> bf16 (RNE)      kept in registers; the S^T accumulator layout is
-//                          the B operand of O^T = V^T P^T once the keys of
-//                          each MFMA are taken in the accumulator's order.
-//                          The row sum l accumulates the fp32 P, so lse keeps
-//                          fp32 accuracy
-//     O^T += V^T P^T       32x32x16 bf16 MFMA; V stays row-major in LDS and
-//                          its transposed operand comes from ds_read_b64_tr_b16
+//   one workgroup = 256 query rows of one (batch, query head): 8 waves of 32
+//   rows, one workgroup per CU.  Waves w and w + 4 share a SIMD; waves 0-3
+//   (group 0) and 4-7 (group 1) run half a step apart, so that while one
+//   wave of a SIMD works on the matrix cores the other mostly works on the
+//   vector ALU.  K/V tiles of 64 keys stream through LDS (two slots each for
+//   K and V) by buffer loads that write LDS directly (no register staging;
+//   rows past the end of the keys read as zero).  One K/V tile load serves
+//   all 256 rows, half the load traffic of 128-row workgroups.
+//
+//   Step s (one workgroup barrier per step):
+//     matrix part   O^T += V^T P^T for tile s-1, then S^T = K Q^T for tile s
+//                   (32x32x16 bf16 MFMAs; one lane = one query row; V^T from
+//                   ds_read_b64_tr_b16).  The LDS reads run ahead of the
+//                   products, and this part runs at raised wave priority.
+//     softmax part  of tile s: mask (only tiles crossing the diagonal or the
+//                   end of the keys), row max (in-lane plus one exchange of the
+//                   wave halves), lazy rescale (the exponent reference m only
+//                   moves when the row max has grown by more than 2^8),
+//                   P = 2^(s c - m): one FMA + one v_exp_f32 per score, rounded
+//                   to bf16 (RNE) in the layout of the PV operand; the row sum
+//                   adds the fp32 P, so lse keeps fp32 accuracy
+//     group 0 runs [matrix(s), softmax(s)], group 1 [softmax(s-1), matrix(s)];
+//     every wave issues its share of the loads of K(s+1) and V(s), which land
+//     by the step's closing barrier.
+//   Waves compute every tile of the workgroup; tiles past a wave's diagonal
+//   are fully masked and contribute P = 0.
 //   Epilogue: O = O / l rounded to bf16, lse = (m + log2 l) * ln 2.
 //
 // LDS tiles are row-major with 16-byte chunks XOR-swizzled per row so that
 // both the K row reads and the transposing V reads spread over all banks.
+//
+// Paged keys and values (chunked prefill, "抱infra脚" Paged Attention and
+// Chunked Prefill): the 64 keys of a tile are 4 cache blocks of 16 tokens;
+// wave w loads its 8 rows of block 4 j + w / 2, whose physical id comes
+// through the scalar cache one step ahead.
 //
 // Grid: one workgroup per (q-tile, query head, batch).  Workgroup ids are
 // mapped so that the longest causal q-tiles start first and all query heads
@@ -47,21 +58,25 @@
 namespace attn {
 namespace {
 
-constexpr int kBR = 128;      // query rows per workgroup
+constexpr int kBR = 256;      // query rows per workgroup
 constexpr int kBC = 64;       // keys per K/V tile
 constexpr int kBS = 16;       // tokens per cache block (paged keys and values)
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
 
 // An empty volatile asm statement: placed inside a rarely taken branch it
 // keeps the compiler from turning the branch into unconditional arithmetic.
 __device__ __forceinline__ void keep_branch() { asm volatile(""); }
 
+// Instruction-class masks of the scheduling-group builtin.
+constexpr int kSchedMfma = 0x008, kSchedVmem = 0x010, kSchedDsRead = 0x100;
+#define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+
 template <int D>
 struct Tile {
     static constexpr int cpr = D / 8;                     // 16-byte chunks per row
     static constexpr int elems = kBC * D;                 // bf16 elements per K or V tile
-    static constexpr int loads_per_wave = kBC * cpr / 64 / kWaves;   // 1 KiB LDS-direct loads
+    static constexpr int lpw = kBC * cpr / 64 / kWaves;   // 1 KiB LDS-direct loads per wave per K or V tile
     // Physical chunk of logical chunk c in row r.
     static __device__ __forceinline__ int swz(int r, int c)
     {
@@ -102,13 +117,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
 {
     using T = Tile<D>;
-    __shared__ __attribute__((aligned(1024))) uint16_t k_st0[T::elems];
-    __shared__ __attribute__((aligned(1024))) uint16_t v_st0[T::elems];
-    __shared__ __attribute__((aligned(1024))) uint16_t k_st1[T::elems];
-    __shared__ __attribute__((aligned(1024))) uint16_t v_st1[T::elems];
+    // Distinct arrays per slot, so that the compiler's wait for a slot's
+    // LDS-direct loads never covers the loads in flight to the other slot.
+    __shared__ __attribute__((aligned(1024))) uint16_t k_s0[T::elems];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_s1[T::elems];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_s0[T::elems];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_s1[T::elems];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave >> 2;
     const int l32 = lane & 31, h = lane >> 5;
 
     int b, hq, qt;
@@ -133,12 +151,17 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
 
     int kend = Sk;                      // keys [0, kend) may be visible to this workgroup
     if (CAUSAL) kend = min(Sk, min(a.Sq, i0 + kBR) + diag);
-    const int ntiles = kend > 0 ? (kend + kBC - 1) / kBC : 0;
+    const int n = kend > 0 ? (kend + kBC - 1) / kBC : 0;
+    // Tiles before first_masked are fully visible to every row of this wave.
+    int first_masked = Sk / kBC;
+    if (CAUSAL) first_masked = min(first_masked, max(0, (q0 + diag + 1) / kBC));
 
     // Exponent scale c = scale * log2(e), made non-negative by flipping the
-    // sign of Q (exact in bf16) when the caller's scale is negative.
+    // sign of Q (exact in bf16) when the caller's scale is negative, and at
+    // least FLT_MIN: a masked score (-inf) then always maps to 2^-inf = 0,
+    // and a zero scale still gives uniform weights.
     const bool neg = a.scale_log2 < 0.f;
-    const float c = neg ? -a.scale_log2 : a.scale_log2;
+    const float c = fmaxf(neg ? -a.scale_log2 : a.scale_log2, 1.17549435e-38f);
 
     // Q^T operand of S^T = K Q^T: lane (h, l32) holds q[my_q][16ks + 8h .. +8].
     u32x4_t qf[D / 16];
@@ -157,71 +180,78 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
 
     // ---- K/V streaming: buffer loads that write LDS directly ------------
     const uint32_t row_bytes = (uint32_t)(a.Hkv * D * 2);
+    // Per-lane source offsets (bytes) of the 16-byte chunks this lane's loads
+    // deliver: load i of wave w fills LDS chunk slots (w * lpw + i) * 64 + lane,
+    // rows 8 w .. 8 w + 7 of the tile.  Contiguous: relative to the tile's
+    // first key; paged: relative to the first token of cache block w / 2.
+    uint32_t src_off[T::lpw];
+#pragma unroll
+    for (int i = 0; i < T::lpw; ++i) {
+        const int slot = (wave * T::lpw + i) * 64 + lane;
+        const int r = slot / T::cpr, p = slot % T::cpr;
+        src_off[i] = (uint32_t)(PAGED ? r - kBS * (wave >> 1) : r) * row_bytes + (uint32_t)T::swz(r, p) * 16u;
+    }
+    auto load_slot = [&](__amdgpu_buffer_rsrc_t r, uint16_t *dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < T::lpw; ++i) buffer_load_lds16(r, dst + (wave * T::lpw + i) * 64 * 8, src_off[i]);
+    };
+
+    // Contiguous keys: descriptors over [first key of tile j, end of the keys).
     const size_t head_off = PAGED ? 0 : ((size_t)b * a.Sk * a.Hkv + hk) * D;      // elements
     const char *kbase = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k) + head_off);
     const char *vbase = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.v) + head_off);
-    // Bytes from this head's first key to the end of its last key row.
     const uint32_t span = Sk > 0 ? (uint32_t)(((size_t)(Sk - 1) * a.Hkv * D + D) * 2) : 0u;
+    auto rsrc_tile = [&](const char *base, int j) __attribute__((always_inline)) {
+        const uint32_t start = (uint32_t)(j * kBC) * row_bytes;
+        const uint32_t left = (j < n && span > start) ? span - start : 0u;
+        return make_rsrc(base + start, left);
+    };
 
-    // Per-lane source offsets (bytes, relative to the tile's first key) of the
-    // 16-byte chunks this lane's LDS-direct loads deliver: load i of wave w
-    // fills LDS chunk slots (w * loads + i) * 64 + lane.
-    uint32_t src_off[T::loads_per_wave];
-#pragma unroll
-    for (int i = 0; i < T::loads_per_wave; ++i) {
-        const int slot = (wave * T::loads_per_wave + i) * 64 + lane;
-        const int r = slot / T::cpr, p = slot % T::cpr;
-        const int cl = T::swz(r, p);                      // swz is an involution
-        // Paged: the wave's 16 rows are one cache block; offsets are relative
-        // to this head's slice of that block's first token.
-        src_off[i] = (uint32_t)(PAGED ? r - kBS * wave : r) * row_bytes + (uint32_t)cl * 16u;
-    }
-
-    // Paged: wave w loads cache block 4 j + w of tile j (its 16 rows).  The
-    // physical block ids come through the scalar cache one tile ahead.
+    // Paged keys: wave w's cache block of tile t is 4 t + w / 2; its physical
+    // id is looked up one step ahead through the scalar cache.
     const int n_lblocks = (Sk + kBS - 1) / kBS;
     const int32_t __attribute__((address_space(4))) *tb =
         (const int32_t __attribute__((address_space(4))) *)(a.block_table + (PAGED ? (size_t)b * a.max_blocks : 0));
-    int phys_next = (PAGED && wave < n_lblocks) ? tb[wave] : 0;
     const uint32_t blk_bytes = (uint32_t)kBS * row_bytes;
-
-    auto issue_tile = [&](int j, uint16_t *ks, uint16_t *vs) __attribute__((always_inline)) {
-        __amdgpu_buffer_rsrc_t rk, rv;
+    // Rows of tile t that this wave's block holds (0 past the keys or past
+    // the workgroup's tiles).
+    auto block_rows = [&](int t) __attribute__((always_inline)) {
+        const int lb = (kBC / kBS) * t + (wave >> 1);
+        return (t < n) & (lb < n_lblocks) ? min(kBS, Sk - kBS * lb) : 0;
+    };
+    // Physical id of this wave's block of tile t, read through the scalar
+    // cache at an index clamped into the table row (the value only matters
+    // when the block holds rows).
+    auto lookup = [&](int t) __attribute__((always_inline)) {
+        return (PAGED && a.max_blocks > 0) ? tb[min((kBC / kBS) * t + (wave >> 1), a.max_blocks - 1)] : 0;
+    };
+    // Descriptor of this wave's block of tile t with physical id p; an id
+    // outside the pool marks the sequence bad and reads nothing.
+    auto rsrc_block = [&](const void *cache, int t, int p) __attribute__((always_inline)) {
+        const int rows = block_rows(t);
+        // bitwise, not short-circuit, logic: straight-line scalar code
+        const bool wrong = (rows > 0) & ((p < 0) | (p >= a.num_blocks));
+        bad = bad | wrong;
+        const bool use = (rows > 0) & !wrong;
+        const size_t off = use ? (size_t)(uint32_t)p * blk_bytes + (size_t)hk * D * 2 : 0;
+        const uint32_t num = use ? (uint32_t)(rows - 1) * row_bytes + D * 2 : 0u;
+        return make_rsrc(static_cast<const char *>(cache) + off, num);
+    };
+    // Step s loads K(s+1) and V(s) through descriptors made at the end of the
+    // previous step (scalar work kept out of the matrix part); the block ids
+    // are read one step before the descriptors need them.
+    int id_a = lookup(1), id_b = lookup(2);          // tiles s + 1 and s + 2 at step s
+    __amdgpu_buffer_rsrc_t desc_k = rsrc_block(a.k, 1, id_a), desc_v = rsrc_block(a.v, 0, lookup(0));
+    auto advance = [&](int s) __attribute__((always_inline)) {
         if constexpr (PAGED) {
-            const int lb = (kBC / kBS) * j + wave;
-            const int p = phys_next;
-            phys_next = lb + kBC / kBS < n_lblocks ? tb[lb + kBC / kBS] : 0;
-            int valid = min(kBS, Sk - kBS * lb);
-            long long phys = 0;
-            if (valid > 0) {
-                if (p < 0 || p >= a.num_blocks) {
-                    bad = true;
-                    valid = 0;
-                } else {
-                    phys = p;
-                }
-            } else {
-                valid = 0;
-            }
-            const size_t off = (size_t)phys * blk_bytes + (size_t)hk * D * 2;
-            const uint32_t num = valid > 0 ? (uint32_t)(valid - 1) * row_bytes + D * 2 : 0u;
-            rk = make_rsrc(static_cast<const char *>(a.k) + off, num);
-            rv = make_rsrc(static_cast<const char *>(a.v) + off, num);
-        } else {
-            const uint32_t start = (uint32_t)(j * kBC) * row_bytes;
-            const uint32_t left = span > start ? span - start : 0u;
-            rk = make_rsrc(kbase + start, left);
-            rv = make_rsrc(vbase + start, left);
-        }
-#pragma unroll
-        for (int i = 0; i < T::loads_per_wave; ++i) {
-            const int chunk0 = (wave * T::loads_per_wave + i) * 64;      // uniform
-            buffer_load_lds16(rk, ks + chunk0 * 8, src_off[i]);
-            buffer_load_lds16(rv, vs + chunk0 * 8, src_off[i]);
+            desc_v = rsrc_block(a.v, s + 1, id_a);
+            desc_k = rsrc_block(a.k, s + 2, id_b);
+            id_a = id_b;
+            id_b = lookup(s + 3);
         }
     };
 
-    // ---- per-lane LDS read offsets (elements) --------------------------------
+    // ---- per-lane LDS read offsets (elements) ----------------------------
     // K operand (S^T A operand): row l32 (+32 kb), chunk 2 kk + h.
     int k_rd[D / 16];
 #pragma unroll
@@ -239,7 +269,7 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
             v_rd[t][db] = r * D + T::swz(r, d >> 3) * 8 + (d & 7);
         }
 
-    // ---- per-lane softmax state and output accumulator ----------------
+    // ---- per-lane softmax state and accumulators --------------------------
     f32x16_t oacc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -248,45 +278,115 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
     float m = kNegInf;      // exponent reference (log2 domain) of this row
     float lsum = 0.f;       // this lane's share of the row sum
     const f32x16_t zero16 = {};
+    f32x16_t sc[2];          // S^T of a tile between its QK and its softmax
+    u32x4_t pk[2][2];        // P of a tile between its softmax and its PV
 
-    // Tiles before `first_masked` are fully visible to every row of this wave.
-    int first_masked = Sk / kBC;                         // full tiles inside the sequence
-    if (CAUSAL) first_masked = min(first_masked, max(0, (q0 + diag + 1) / kBC));
+    constexpr int NMF = D / 8;                 // MFMAs per tile and wave, for QK and for PV
+    constexpr int PVA = 4, QKA = 4;            // products the LDS reads run ahead
 
-    // One code path for every tile: masking is a uniform branch around the
-    // few instructions that need it, so the output accumulator keeps its
-    // registers across tiles.
-    auto run_tile = [&](const uint16_t *ks, const uint16_t *vs, int j, auto masked_tag) __attribute__((always_inline)) {
-        constexpr bool masked = decltype(masked_tag)::value;
-        const int kv0 = j * kBC;
-        // S^T = K Q^T (both 32-key halves; on diagonal tiles a half may be
-        // fully masked, which the mask below handles)
-        f32x16_t s[2];
+    auto read_v = [&](const uint16_t *vs, u32x4_t (&vf)[2][2][D / 32]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = mfma_32x32x16_bf16(*reinterpret_cast<const u32x4_t *>(ks + k_rd[0] + 32 * kb * D), qf[0], zero16);
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kk = 1; kk < D / 16; ++kk) {
-                const u32x4_t kop = *reinterpret_cast<const u32x4_t *>(ks + k_rd[kk] + 32 * kb * D);
-                s[kb] = mfma_32x32x16_bf16(kop, qf[kk], s[kb]);
-            }
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const int e = (32 * kb + 16 * cc) * D;
+                    const u32x2_t lo = lds_read_tr16(vs + v_rd[0][db] + e);
+                    const u32x2_t hi = lds_read_tr16(vs + v_rd[1][db] + e);
+                    vf[kb][cc][db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+                }
+    };
+    auto read_k = [&](const uint16_t *ks, u32x4_t (&kf)[D / 16][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) kf[kk][kb] = *reinterpret_cast<const u32x4_t *>(ks + k_rd[kk] + 32 * kb * D);
+    };
+    // O^T += V^T P^T; the S^T accumulator layout is the B operand once the
+    // keys of each MFMA are taken in the accumulator's order.
+    auto pv = [&](const u32x4_t (&vf)[2][2][D / 32]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) oacc[db] = mfma_32x32x16_bf16(vf[kb][cc][db], pk[kb][cc], oacc[db]);
+    };
+    // S^T = K Q^T, both 32-key halves of the tile.
+    auto qk = [&](const u32x4_t (&kf)[D / 16][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) sc[kb] = mfma_32x32x16_bf16(kf[kk][kb], qf[kk], kk == 0 ? zero16 : sc[kb]);
+    };
+
+    // Matrix part of a steady step: PV of the previous tile, then QK of this
+    // one; a single code path (no branch touches the accumulators).
+    auto mma_full = [&](const uint16_t *ks, const uint16_t *vs, auto &&issue) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
+        u32x4_t vf[2][2][D / 32];
+        u32x4_t kf[D / 16][2];
+        read_v(vs, vf);
+        read_k(ks, kf);
+        issue();
+        pv(vf);
+        qk(kf);
+        SCHED_GROUP(kSchedDsRead, 2 * PVA);
+        SCHED_GROUP(kSchedVmem, 4 * T::lpw);
+#pragma unroll
+        for (int i = 0; i < NMF - PVA; ++i) {
+            SCHED_GROUP(kSchedMfma, 1);
+            SCHED_GROUP(kSchedDsRead, 2);
         }
-        if constexpr (masked) {
+#pragma unroll
+        for (int i = 0; i < PVA; ++i) {
+            SCHED_GROUP(kSchedMfma, 1);
+            if (i < QKA) SCHED_GROUP(kSchedDsRead, 1);
+        }
+#pragma unroll
+        for (int i = 0; i < NMF - QKA; ++i) {
+            SCHED_GROUP(kSchedMfma, 1);
+            SCHED_GROUP(kSchedDsRead, 1);
+        }
+        SCHED_GROUP(kSchedMfma, QKA);
+        __builtin_amdgcn_s_setprio(0);
+    };
+    auto mma_qk_only = [&](const uint16_t *ks, auto &&issue) __attribute__((always_inline)) {
+        u32x4_t kf[D / 16][2];
+        read_k(ks, kf);
+        issue();
+        qk(kf);
+    };
+    auto mma_pv_only = [&](const uint16_t *vs) __attribute__((always_inline)) {
+        u32x4_t vf[2][2][D / 32];
+        read_v(vs, vf);
+        pv(vf);
+    };
+
+    // Softmax of tile s.
+    auto softmax = [&](int s) __attribute__((always_inline)) {
+        if (s >= first_masked) {
+            keep_branch();
+            // last visible key offset in the tile, less this lane's 4 h, so that
+            // every compare is against an inline constant
+            const int lim = (CAUSAL ? min(Sk - 1, my_q + diag) : Sk - 1) - s * kBC - 4 * h;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int key = kv0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
-                    const bool vis = key < Sk && (!CAUSAL || key <= my_q + diag);
-                    s[kb][v] = vis ? s[kb][v] : kNegInf;
+                    const int ko = 32 * kb + 8 * (v >> 2) + (v & 3);
+                    sc[kb][v] = ko <= lim ? sc[kb][v] : kNegInf;
                 }
         }
-        // Row max of the raw scores (c >= 0, so scaling preserves order).
-        float mraw = kNegInf;
+        // Row max of the raw scores (c > 0, so scaling preserves order), as
+        // four independent partial maxima.
+        float mp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, s[kb][v]);
+            for (int v = 0; v < 16; ++v) mp[2 * kb + (v >> 3)] = fmaxf(mp[2 * kb + (v >> 3)], sc[kb][v]);
+        float mraw = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
         mraw = pair_max_halves(mraw);
         const float mx = mraw == kNegInf ? kNegInf : mraw * c;
         const float m_new = fmaxf(m, mx);
@@ -300,68 +400,81 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
             for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
         }
         const float nm = (m == kNegInf) ? 0.f : -m;
-        // Exponents s c - m; masked scores stay -inf (also when c == 0).
-        float x[2][16];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) x[kb][v] = __builtin_fmaf(s[kb][v], c, nm);
-        if constexpr (masked) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) x[kb][v] = s[kb][v] == kNegInf ? kNegInf : x[kb][v];
-        }
-        // P = 2^x -> bf16 pairs; the row sum adds the fp32 values.
-        u32x4_t pk[2][2];
+        // P = 2^(s c - m) -> bf16 pairs; the row sum adds the fp32 values.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float p0 = exp2_fast(x[kb][8 * cc + 2 * e]), p1 = exp2_fast(x[kb][8 * cc + 2 * e + 1]);
+                    const float p0 = exp2_fast(__builtin_fmaf(sc[kb][8 * cc + 2 * e], c, nm));
+                    const float p1 = exp2_fast(__builtin_fmaf(sc[kb][8 * cc + 2 * e + 1], c, nm));
                     pk[kb][cc][e] = pack_bf16x2(p0, p1);
                     lsum += p0 + p1;
                 }
-        // O^T += V^T P^T
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                const int kbase_el = (32 * kb + 16 * cc) * D;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const u32x2_t lo = lds_read_tr16(vs + v_rd[0][db] + kbase_el);
-                    const u32x2_t hi = lds_read_tr16(vs + v_rd[1][db] + kbase_el);
-                    const u32x4_t vop = {lo[0], lo[1], hi[0], hi[1]};
-                    oacc[db] = mfma_32x32x16_bf16(vop, pk[kb][cc], oacc[db]);
-                }
-            }
-        }
     };
 
-    // Tiles [0, fm) need no mask for this wave: they run in a branch-free
-    // loop over the two static stages.  The remaining tiles (those crossing
-    // the diagonal or the end of the keys, and an odd leftover) run through
-    // the masked body.  Every wave passes one barrier per tile either way.
-    const int fm = min(first_masked, ntiles);
-    if (ntiles > 0) issue_tile(0, k_st0, v_st0);
+    // ---- steps s = 0..n: K(s) in k_s[s & 1], V(s) in v_s[s & 1] ----------
+    // Step s loads K(s+1) and V(s) (slots freed by the previous step's
+    // barrier); they land by step s's closing barrier.
+    auto issue = [&](int s, uint16_t *k_ld, uint16_t *v_ld) __attribute__((always_inline)) {
+        if constexpr (PAGED) {
+            load_slot(desc_k, k_ld);
+            load_slot(desc_v, v_ld);
+        } else {
+            load_slot(rsrc_tile(kbase, s + 1), k_ld);
+            load_slot(rsrc_tile(vbase, s), v_ld);
+        }
+    };
+    if constexpr (PAGED)
+        load_slot(rsrc_block(a.k, 0, lookup(0)), k_s0);
+    else
+        load_slot(rsrc_tile(kbase, 0), k_s0);
     __syncthreads();
-    int j = 0;
-    for (; j + 1 < fm; j += 2) {
-        issue_tile(j + 1, k_st1, v_st1);
-        run_tile(k_st0, v_st0, j, std::false_type{});
-        __syncthreads();
-        if (j + 2 < ntiles) issue_tile(j + 2, k_st0, v_st0);
-        run_tile(k_st1, v_st1, j + 1, std::false_type{});
-        __syncthreads();
-    }
-    for (; j < ntiles; ++j) {
-        uint16_t *ks = (j & 1) ? k_st1 : k_st0, *vs = (j & 1) ? v_st1 : v_st0;
-        if (j + 1 < ntiles) issue_tile(j + 1, (j & 1) ? k_st0 : k_st1, (j & 1) ? v_st0 : v_st1);
-        run_tile(ks, vs, j, std::true_type{});
-        __syncthreads();
+    if (n > 0) {
+        auto body0 = [&](int s, const uint16_t *ks, const uint16_t *vs, uint16_t *k_ld, uint16_t *v_ld)
+            __attribute__((always_inline)) {
+            mma_full(ks, vs, [&]() __attribute__((always_inline)) { issue(s, k_ld, v_ld); });
+            softmax(s);
+            advance(s);
+            __syncthreads();
+        };
+        auto body1 = [&](int s, const uint16_t *ks, const uint16_t *vs, uint16_t *k_ld, uint16_t *v_ld)
+            __attribute__((always_inline)) {
+            issue(s, k_ld, v_ld);
+            softmax(s - 1);
+            mma_full(ks, vs, []() {});
+            advance(s);
+            __syncthreads();
+        };
+        if (grp == 0) {
+            mma_qk_only(k_s0, [&]() __attribute__((always_inline)) { issue(0, k_s1, v_s0); });
+            softmax(0);
+            advance(0);
+            __syncthreads();
+            int s = 1;
+            for (; s + 1 < n; s += 2) {
+                body0(s, k_s1, v_s0, k_s0, v_s1);
+                body0(s + 1, k_s0, v_s1, k_s1, v_s0);
+            }
+            if (s < n) body0(s, k_s1, v_s0, k_s0, v_s1);
+            mma_pv_only((n & 1) ? v_s0 : v_s1);
+            __syncthreads();
+        } else {
+            issue(0, k_s1, v_s0);
+            mma_qk_only(k_s0, []() {});
+            advance(0);
+            __syncthreads();
+            int s = 1;
+            for (; s + 1 < n; s += 2) {
+                body1(s, k_s1, v_s0, k_s0, v_s1);
+                body1(s + 1, k_s0, v_s1, k_s1, v_s0);
+            }
+            if (s < n) body1(s, k_s1, v_s0, k_s0, v_s1);
+            softmax(n - 1);
+            mma_pv_only((n & 1) ? v_s0 : v_s1);
+            __syncthreads();
+        }
     }
 
     // ---- epilogue ----------------------------------------------------------
