@@ -90,6 +90,8 @@ PREFILL_BF16_CASES = [
     (2, 300, 300, 16, 4, 128, True),    # (batch, KV head) pairs a multiple of 8
     (1, 384, 384, 32, 8, 128, True),
     (1, 130, 70, 4, 2, 128, False),
+    (1, 512, 512, 8, 8, 64, True),      # two full 256-row workgroups, D = 64
+    (2, 5, 1000, 4, 2, 128, False),     # few queries, many keys: one busy wave per workgroup
 ]
 
 
