@@ -34,8 +34,10 @@
 //     group 0 runs [matrix(s), softmax(s)], group 1 [softmax(s-1), matrix(s)];
 //     every wave issues its share of the loads of K(s+1) and V(s), which land
 //     by the step's closing barrier.
-//   Waves compute every tile of the workgroup; tiles past a wave's diagonal
-//   are fully masked and contribute P = 0.
+//   A wave computes the tiles up to its own last visible key; for the
+//   remaining steps of its workgroup (past its diagonal) it only issues its
+//   share of the loads.  These are separate loops, so no branch inside a
+//   step ever touches the output accumulators.
 //   Epilogue: O = O / l rounded to bf16, lse = (m + log2 l) * ln 2.
 //
 // LDS tiles are row-major with 16-byte chunks XOR-swizzled per row so that
@@ -152,6 +154,12 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
     int kend = Sk;                      // keys [0, kend) may be visible to this workgroup
     if (CAUSAL) kend = min(Sk, min(a.Sq, i0 + kBR) + diag);
     const int n = kend > 0 ? (kend + kBC - 1) / kBC : 0;
+    // Tiles [0, nw) hold keys visible to some row of this wave; from step nw
+    // on the wave only issues its share of the loads (its P would be 0).
+    int kend_w = Sk;
+    if (CAUSAL) kend_w = min(Sk, min(a.Sq, q0 + 32) + diag);
+    if (q0 >= a.Sq) kend_w = 0;
+    const int nw = kend_w > 0 ? (kend_w + kBC - 1) / kBC : 0;
     // Tiles before first_masked are fully visible to every row of this wave.
     int first_masked = Sk / kBC;
     if (CAUSAL) first_masked = min(first_masked, max(0, (q0 + diag + 1) / kBC));
@@ -447,18 +455,42 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
             advance(s);
             __syncthreads();
         };
+        // A step that only issues this wave's loads.
+        auto idle = [&](int s) __attribute__((always_inline)) {
+            if (s & 1)
+                issue(s, k_s0, v_s1);
+            else
+                issue(s, k_s1, v_s0);
+            advance(s);
+            __syncthreads();
+        };
+        const int m_end = min(nw, n);     // steps [1, m_end) run in full
         if (grp == 0) {
             mma_qk_only(k_s0, [&]() __attribute__((always_inline)) { issue(0, k_s1, v_s0); });
             softmax(0);
             advance(0);
             __syncthreads();
             int s = 1;
-            for (; s + 1 < n; s += 2) {
+            for (; s + 1 < m_end; s += 2) {
                 body0(s, k_s1, v_s0, k_s0, v_s1);
                 body0(s + 1, k_s0, v_s1, k_s1, v_s0);
             }
-            if (s < n) body0(s, k_s1, v_s0, k_s0, v_s1);
-            mma_pv_only((n & 1) ? v_s0 : v_s1);
+            if (s < m_end) body0(s++, k_s1, v_s0, k_s0, v_s1);
+            if (s == nw && s < n) {
+                // this wave's last PV (tile nw - 1), then loads only
+                if (s & 1) {
+                    mma_pv_only(v_s0);
+                    issue(s, k_s0, v_s1);
+                } else {
+                    mma_pv_only(v_s1);
+                    issue(s, k_s1, v_s0);
+                }
+                advance(s);
+                __syncthreads();
+                ++s;
+            }
+            for (; s < n; ++s) idle(s);
+            if (nw >= n) mma_pv_only((n & 1) ? v_s0 : v_s1);
             __syncthreads();
         } else {
             issue(0, k_s1, v_s0);
@@ -466,13 +498,27 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
             advance(0);
             __syncthreads();
             int s = 1;
-            for (; s + 1 < n; s += 2) {
+            for (; s + 1 < m_end; s += 2) {
                 body1(s, k_s1, v_s0, k_s0, v_s1);
                 body1(s + 1, k_s0, v_s1, k_s1, v_s0);
             }
-            if (s < n) body1(s, k_s1, v_s0, k_s0, v_s1);
-            softmax(n - 1);
-            mma_pv_only((n & 1) ? v_s0 : v_s1);
+            if (s < m_end) body1(s++, k_s1, v_s0, k_s0, v_s1);
+            if (s == nw && s < n) {
+                if (s & 1)
+                    issue(s, k_s0, v_s1);
+                else
+                    issue(s, k_s1, v_s0);
+                softmax(s - 1);
+                mma_pv_only((s & 1) ? v_s0 : v_s1);
+                advance(s);
+                __syncthreads();
+                ++s;
+            }
+            for (; s < n; ++s) idle(s);
+            if (nw >= n) {
+                softmax(n - 1);
+                mma_pv_only((n & 1) ? v_s0 : v_s1);
+            }
             __syncthreads();
         }
     }
