@@ -1,0 +1,126 @@
+"""Parity of the HIP path with the fp64 oracle on seeded random shapes.
+
+The hand-picked cases of test_parity_gpu.py cover the edges one at a time;
+these draw batch, lengths (ragged and unaligned), head layout, head_dim,
+causality and split counts from a seeded generator, so that combinations
+nobody picked are exercised too.  Same tolerances as the other parity tests
+(bf16 output max-abs 2e-2, mean-abs 2e-3; lse max-abs 1e-4).  Sizes are
+capped so that the oracle finishes each case in well under a second.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.helpers import BF16_LSE_ABS, BF16_MAX_ABS, BF16_MEAN_ABS, check_lse, check_o, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+MAX_PAIRS = 20_000_000      # (query row, key, query head) triples per case
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def afa(cuda):
+    import attention_flash_fwd_amd as afa_mod
+    from attention_flash_fwd_amd import _lib
+    _lib.load()
+    return afa_mod
+
+
+def heads(rng, max_hq=32):
+    while True:
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 4, 8, 16]))
+        if hkv * g <= max_hq:
+            return hkv * g, hkv
+
+
+def oracle_paged(inp, q, causal, scale):
+    qn = to_np(q)
+    os_, ls_ = [], []
+    for b in range(len(inp.ctx)):
+        kb, vb = inp.logical_kv(b, device="cpu")
+        o, l = oracle.attention(qn[b:b + 1], kb.float().numpy()[None], vb.float().numpy()[None], causal, scale)
+        os_.append(o[0])
+        ls_.append(l[0])
+    return np.stack(os_), np.stack(ls_)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_prefill_random(afa, seed):
+    from attention_flash_fwd_amd import inputs
+    rng = np.random.default_rng(9100 + seed)
+    B = int(rng.integers(1, 4))
+    Hq, Hkv = heads(rng)
+    D = int(rng.choice([64, 128]))
+    causal = bool(rng.random() < 0.7)
+    Sq = int(rng.integers(1, 700))
+    Sk = Sq if rng.random() < 0.5 else int(rng.integers(1, 700))
+    while B * Hq * Sq * Sk > MAX_PAIRS:
+        Sq, Sk = max(1, Sq * 3 // 4), max(1, Sk * 3 // 4)
+    say(f"case random prefill seed{seed}: B{B} Sq{Sq} Sk{Sk} Hq{Hq} Hkv{Hkv} D{D} causal{causal}")
+    q, k, v = inputs.prefill_inputs(B, Sq, Sk, Hq, Hkv, D, torch.bfloat16, 500 + seed, device="cpu")
+    scale = 1 / math.sqrt(D)
+    o, lse = afa.prefill(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(to_np(q), to_np(k), to_np(v), causal, scale)
+    check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse), l_ref, BF16_LSE_ABS)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_prefill_paged_random(afa, seed):
+    from attention_flash_fwd_amd import inputs
+    rng = np.random.default_rng(9200 + seed)
+    nseq = int(rng.integers(1, 5))
+    Hq, Hkv = heads(rng)
+    D = int(rng.choice([64, 128]))
+    causal = bool(rng.random() < 0.7)
+    ctx = [int(rng.integers(0, 900)) for _ in range(nseq)]
+    Sq = int(rng.integers(1, 400))
+    while nseq * Hq * Sq * max(max(ctx), 1) > MAX_PAIRS:
+        Sq = max(1, Sq * 3 // 4)
+        ctx = [c * 3 // 4 for c in ctx]
+    say(f"case random prefill_paged seed{seed}: ctx{ctx} Sq{Sq} Hq{Hq} Hkv{Hkv} D{D} causal{causal}")
+    inp = inputs.decode_inputs(ctx, Hq, Hkv, D, seed=600 + seed, device="cuda", spare_blocks=2)
+    q = inputs.chunk_queries(nseq, Sq, Hq, D, seed=600 + seed, device="cuda")
+    scale = 1 / math.sqrt(D)
+    o, lse = afa.prefill_paged(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                               causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle_paged(inp, q, causal, scale)
+    check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse), l_ref, BF16_LSE_ABS)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_decode_random(afa, seed):
+    from attention_flash_fwd_amd import inputs
+    rng = np.random.default_rng(9300 + seed)
+    nseq = int(rng.integers(1, 9))
+    Hq, Hkv = heads(rng, max_hq=64)
+    D = int(rng.choice([64, 128]))
+    T = int(rng.integers(1, 5))
+    while (Hq // Hkv) * T > 64:
+        T -= 1
+    ctx = [int(rng.integers(1, 3000)) for _ in range(nseq)]
+    splits = int(rng.choice([0, 1, 2, 3, 5, 8, 13, 32]))
+    say(f"case random decode seed{seed}: ctx{ctx} T{T} Hq{Hq} Hkv{Hkv} D{D} splits{splits}")
+    inp = inputs.decode_inputs(ctx, Hq, Hkv, D, seed=700 + seed, device="cuda", spare_blocks=2)
+    q = inputs.chunk_queries(nseq, T, Hq, D, seed=700 + seed, device="cuda")
+    scale = 1 / math.sqrt(D)
+    o, lse = afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                    num_splits=splits, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle_paged(inp, q, True, scale)
+    check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse), l_ref, BF16_LSE_ABS)
