@@ -49,9 +49,10 @@
 // through the scalar cache one step ahead.
 //
 // Grid: one workgroup per (q-tile, query head, batch).  Workgroup ids are
-// mapped so that the longest causal q-tiles start first and all query heads
-// of one (batch, KV head) land on the same XCD (ids go round-robin over the
-// 8 XCDs), where its K/V stays in that XCD's L2.
+// mapped so that all query heads of one (batch, KV head) land on the same
+// XCD (ids go round-robin over the 8 XCDs), each XCD works through its
+// (batch, KV head) pairs one at a time, and within a pair the longest
+// causal q-tiles start first: the pair's K/V stays in that XCD's L2.
 #include <type_traits>
 
 #include "gfx950.hpp"
@@ -97,11 +98,15 @@ __device__ __forceinline__ void map_workgroup(int L, const PrefillArgs &a, int n
     int qt_rev, g, hg;
     if (groups % 8 == 0) {
         const int xcd = L & 7, r = L >> 3;
-        const int per = (groups >> 3) * G;          // workgroups per XCD per q-tile
-        qt_rev = r / per;
-        const int rem = r - qt_rev * per;
-        g = xcd + 8 * (rem / G);
+        // group-major on each XCD: all q-tiles of one (batch, KV head) pair,
+        // heaviest first, before the next pair, so that one pair's K/V is
+        // the XCD's L2 working set
+        const int per = n_qtiles * G;               // workgroups of one pair
+        const int gi = r / per;
+        const int rem = r - gi * per;
+        qt_rev = rem / G;
         hg = rem % G;
+        g = xcd + 8 * gi;
     } else {
         const int per = groups * G;
         qt_rev = L / per;
