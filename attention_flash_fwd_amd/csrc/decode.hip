@@ -20,7 +20,10 @@
 //     O^T (D x 16 columns)       += V^T P^T  D/16 x 16x16x16 bf16 MFMA
 //   New token t sees the keys up to position ctx - T + t; that limit is only
 //   checked on the blocks that reach past ctx - T.  More than 16 columns are
-//   split over column tiles, one workgroup each.
+//   split over column tiles of 16; one workgroup computes up to four tiles
+//   from the same LDS copy of each block (every K and V^T fragment it reads
+//   feeds one product per tile), and more tiles than that go to several
+//   workgroups.
 //   The score accumulator of a lane (4 tokens of one head) is exactly the
 //   B operand the 16x16x16 product wants, and the V^T operand comes from one
 //   transposing LDS read per 16 rows of d.  Cache slots past the chunk end
@@ -39,6 +42,11 @@ namespace {
 
 constexpr int kBS = 16;         // tokens per cache block
 constexpr int kWaves = 4;
+// 16-column tiles one split workgroup computes at most: as many as the
+// per-tile Q operands and accumulators (3 D / 8 + 2 registers a tile) leave
+// room for within 256 registers.
+template <int D>
+constexpr int max_tiles() { return D == 128 ? 3 : 4; }
 constexpr int kThreads = 64 * kWaves;
 constexpr uint32_t kOutside = 0x80000000u;   // buffer offset past any block: reads zero
 
@@ -132,16 +140,20 @@ __device__ __forceinline__ void convert_v(const uint8_t *vs, uint8_t *cv, int la
     }
 }
 
-// One block: scores, online softmax, PV.  ks holds K with EB-byte elements;
-// vs holds V as bf16 (for fp8 caches, the converted scratch copy).
-template <int D, int EB>
+// One block: scores, online softmax, PV, for NCT column tiles at once.  ks
+// holds K with EB-byte elements; vs holds V as bf16 (for fp8 caches, the
+// converted scratch copy).  Each K fragment and each V^T fragment read from
+// LDS feeds the products of every tile.
+template <int D, int EB, int NCT>
 __device__ __forceinline__ void compute_block(const uint8_t *ks, const uint8_t *vs, int valid,
-                                              bool causal, int tok0, int lim,
-                                              float scale_log2, int l16, int g, WaveState<D> &w)
+                                              bool causal, int tok0, const int (&lim)[NCT],
+                                              float scale_log2, int l16, int g, WaveState<D> (&w)[NCT])
 {
     using Gm = Geom<D, 2>;
     using GK = Geom<D, EB>;
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t s[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) s[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     {
         const uint8_t *row = ks + l16 * GK::row_bytes;
         const int sw = GK::swz(l16);
@@ -156,37 +168,53 @@ __device__ __forceinline__ void compute_block(const uint8_t *ks, const uint8_t *
                 const u32x2_t lo = fp8x4_to_bf16(x[0]), hi = fp8x4_to_bf16(x[1]);
                 kf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
             }
-            s = mfma_16x16x32_bf16(kf, w.qf[kk], s);
+#pragma unroll
+            for (int c = 0; c < NCT; ++c) s[c] = mfma_16x16x32_bf16(kf, w[c].qf[kk], s[c]);
         }
     }
-    // Lane (g, l16) holds tokens 4 g + v of head l16.
-    float mx = kNegInf;
+    // Lane (g, l16) holds tokens 4 g + v of head l16.  One branch covers the
+    // lazy rescale of every tile, so the accumulators are touched on a
+    // single path.
+    float m_new[NCT];
+    bool grow_any = false;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const bool vis = 4 * g + v < valid && (!causal || tok0 + 4 * g + v <= lim);
-        const float t = vis ? s[v] * scale_log2 : kNegInf;
-        s[v] = t;
-        mx = fmaxf(mx, t);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(w.m, mx);
-    const bool grow = m_new > w.m + 8.0f;
-    if (wave_any(grow)) {
-        const float alpha = grow ? exp2_fast(w.m - m_new) : 1.0f;
-        w.m = grow ? m_new : w.m;
-        w.l *= alpha;
+    for (int c = 0; c < NCT; ++c) {
+        float mx = kNegInf;
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) w.o[db] *= alpha;
+        for (int v = 0; v < 4; ++v) {
+            const bool vis = 4 * g + v < valid && (!causal || tok0 + 4 * g + v <= lim[c]);
+            const float t = vis ? s[c][v] * scale_log2 : kNegInf;
+            s[c][v] = t;
+            mx = fmaxf(mx, t);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        m_new[c] = fmaxf(w[c].m, mx);
+        grow_any |= m_new[c] > w[c].m + 8.0f;
     }
-    const float mref = (w.m == kNegInf) ? 0.f : w.m;
-    float p[4];
+    if (wave_any(grow_any)) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        p[v] = exp2_fast(s[v] - mref);
-        w.l += p[v];
+        for (int c = 0; c < NCT; ++c) {
+            const bool grow = m_new[c] > w[c].m + 8.0f;
+            const float alpha = grow ? exp2_fast(w[c].m - m_new[c]) : 1.0f;
+            w[c].m = grow ? m_new[c] : w[c].m;
+            w[c].l *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db) w[c].o[db] *= alpha;
+        }
     }
-    const u32x2_t pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+    u32x2_t pk[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+        const float mref = (w[c].m == kNegInf) ? 0.f : w[c].m;
+        float p[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            p[v] = exp2_fast(s[c][v] - mref);
+            w[c].l += p[v];
+        }
+        pk[c] = u32x2_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+    }
 
     // V^T operand: lane (g, i) receives V[4 g + e][16 db + i], e = 0..3, from
     // the rows 4 g + l16 / 4 read by its group.
@@ -197,11 +225,12 @@ __device__ __forceinline__ void compute_block(const uint8_t *ks, const uint8_t *
     for (int db = 0; db < D / 16; ++db) {
         const int chunk = 2 * db + ((l16 & 3) >> 1);
         const u32x2_t vt = lds_read_tr16(reinterpret_cast<const uint16_t *>(vrow + ((chunk ^ vsw) << 4)));
-        w.o[db] = mfma_16x16x16_bf16(vt, pk, w.o[db]);
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) w[c].o[db] = mfma_16x16x16_bf16(vt, pk[c], w[c].o[db]);
     }
 }
 
-template <int D, int EB>
+template <int D, int EB, int NCT>
 __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
 {
     using Gm = Geom<D, EB>;
@@ -222,20 +251,21 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     const int G = a.Hq / a.Hkv;
     const int T = a.T;                  // new tokens per sequence
     const int GT = G * T;               // matrix-core columns in use: (token, head) pairs
-    // Workgroup -> (column tile, chunk, KV head, sequence).  More than 16
-    // columns take several column tiles; the tiles of one (chunk, KV head,
+    // Workgroup -> (tile group, chunk, KV head, sequence).  Columns come in
+    // tiles of 16; a workgroup computes NCT consecutive tiles from one pass
+    // over its chunk.  Past NCT tiles, the groups of one (chunk, KV head,
     // sequence) get ids 8 apart, so they run on the same XCD (ids go
     // round-robin over the 8 XCDs) and share its L2 copy of the K/V blocks.
     const int n_ct = (GT + 15) / 16;
+    const int n_grp = (n_ct + NCT - 1) / NCT;
     const int L = blockIdx.x, r8 = L >> 3;
-    const int ct = r8 % n_ct;
-    const int unit = (r8 / n_ct) * 8 + (L & 7);
+    const int grp = r8 % n_grp;
+    const int unit = (r8 / n_grp) * 8 + (L & 7);
     if (unit >= a.B * a.Hkv * a.splits) return;     // padding of the id space (uniform)
     const int split = unit % a.splits;
     const int hk = (unit / a.splits) % a.Hkv;
     const int b = unit / (a.splits * a.Hkv);
-    const int col0 = 16 * ct;
-    const int NC = min(16, GT - col0);  // columns of this tile
+    const int col_base = 16 * NCT * grp;            // first column of tile 0; tile c starts 16 c later
 
     // Sequence length through the scalar cache: everything derived from it
     // (chunk bounds, trip counts) stays wave-uniform.
@@ -253,24 +283,30 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     // This wave's blocks: chunk blocks wave, wave + 4, ...
     const int nmine = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
 
-    WaveState<D> w;
-    {
-        // Column col = t G + g holds query head hk G + g of new token t.
-        // Columns past G T read the last valid one and are zeroed (no branch
-        // around the load).
-        const bool hv = l16 < NC;
-        const int col = col0 + min(l16, NC - 1);
+    // Column col = t G + g holds query head hk G + g of new token t.  Columns
+    // past G T (a ragged last tile, or whole tiles of the last group) read
+    // the last valid one and are zeroed (no branch around the load); they
+    // are never written out.
+    WaveState<D> w[NCT];
+    int lim[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+        const int want = col_base + 16 * c + l16;
+        const bool hv = want < GT;
+        const int col = min(want, GT - 1);
         const uint16_t *qp = a.q + (((size_t)b * T + col / G) * a.Hq + hk * G + col % G) * D + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             const u32x4_t x = *reinterpret_cast<const u32x4_t *>(qp + 32 * kk);
-            w.qf[kk] = hv ? x : u32x4_t{0, 0, 0, 0};
+            w[c].qf[kk] = hv ? x : u32x4_t{0, 0, 0, 0};
         }
-    }
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) w.o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    w.m = kNegInf;
-    w.l = 0.f;
+        for (int db = 0; db < D / 16; ++db) w[c].o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        w[c].m = kNegInf;
+        w[c].l = 0.f;
+        // New token t sees keys up to position ctx - T + t.
+        lim[c] = ctx - T + col / G;
+    }
 
     // Physical block ids come through the scalar cache (the table is read-only
     // here), one block ahead of their use, so that the loop issues no vector
@@ -314,9 +350,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     auto valid_rows = [&](int j) __attribute__((always_inline)) {
         return min(kBS, t_end - (blk0 + wave + kWaves * j) * kBS);
     };
-    // New token t sees keys up to position ctx - T + t; only blocks reaching
-    // past ctx - T need that check.
-    const int lim = ctx - T + (l16 < NC ? (col0 + l16) / G : 0);
+    // Only blocks reaching past ctx - T need the causal check.
     auto tok0_of = [&](int j) __attribute__((always_inline)) { return (blk0 + wave + kWaves * j) * kBS; };
     auto causal_blk = [&](int j) __attribute__((always_inline)) { return T > 1 && tok0_of(j) + kBS - 1 > ctx - T; };
 
@@ -329,7 +363,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
             __builtin_amdgcn_wave_barrier();
             vb = v_cv[wave];
         }
-        compute_block<D, EB>(ks, vb, valid_rows(j), causal_blk(j), tok0_of(j), lim, a.scale_log2, l16, g, w);
+        compute_block<D, EB, NCT>(ks, vb, valid_rows(j), causal_blk(j), tok0_of(j), lim, a.scale_log2, l16, g, w);
     };
     issue(0, k_s0[wave], v_s0[wave]);
     issue(1, k_s1[wave], v_s1[wave]);
@@ -341,12 +375,16 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     }
 
     // Row sums: lanes g = 0..3 of a head hold disjoint tokens.
-    w.l += __shfl_xor(w.l, 16);
-    w.l += __shfl_xor(w.l, 32);
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+        w[c].l += __shfl_xor(w[c].l, 16);
+        w[c].l += __shfl_xor(w[c].l, 32);
+    }
 
-    // Merge the four wave partials in LDS.  The ring is free once every wave
-    // has drained its loads (the trailing ones past the chunk end fetch
-    // nothing but still write zeros) and passed the barrier.
+    // Merge the four wave partials in LDS, one column tile at a time.  The
+    // ring is free once every wave has drained its loads (the trailing ones
+    // past the chunk end fetch nothing but still write zeros) and passed the
+    // barrier.
     __builtin_amdgcn_s_waitcnt(0);
     const bool any_bad = __syncthreads_or(bad);
     // Wave w's partial O (16 columns x D fp32): bf16 caches put two waves in
@@ -359,42 +397,49 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     };
     float *mo = merge_area(wave);
     float *ml = reinterpret_cast<float *>(EB == 2 ? &k_s1[0][0] : &v_cv[0][0]);   // [wave][16] m, then l
-    if (g == 0) {
-        ml[wave * 16 + l16] = w.m;
-        ml[kWaves * 16 + wave * 16 + l16] = w.l;
-    }
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-        *reinterpret_cast<f32x4_t *>(mo + l16 * D + 16 * db + 4 * g) = w.o[db];
-    __syncthreads();
+    for (int c = 0; c < NCT; ++c) {
+        const int col0 = col_base + 16 * c;
+        if (col0 >= GT) break;                      // uniform: the rest of the group is past the columns
+        const int NC = min(16, GT - col0);          // columns of this tile
+        if (c > 0) __syncthreads();                 // the previous tile's readers are done
+        if (g == 0) {
+            ml[wave * 16 + l16] = w[c].m;
+            ml[kWaves * 16 + wave * 16 + l16] = w[c].l;
+        }
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db)
+            *reinterpret_cast<f32x4_t *>(mo + l16 * D + 16 * db + 4 * g) = w[c].o[db];
+        __syncthreads();
 
-    for (int idx = threadIdx.x; idx < NC * D; idx += kThreads) {
-        const int head = idx / D, d = idx % D;      // head = matrix-core column of this tile
-        const int gcol = col0 + head;
-        float M = kNegInf;
+        for (int idx = threadIdx.x; idx < NC * D; idx += kThreads) {
+            const int head = idx / D, d = idx % D;      // head = matrix-core column of this tile
+            const int gcol = col0 + head;
+            float M = kNegInf;
 #pragma unroll
-        for (int v = 0; v < kWaves; ++v) M = fmaxf(M, ml[v * 16 + head]);
-        float L = 0.f, O = 0.f;
-        if (M != kNegInf) {
+            for (int v = 0; v < kWaves; ++v) M = fmaxf(M, ml[v * 16 + head]);
+            float Ls = 0.f, O = 0.f;
+            if (M != kNegInf) {
 #pragma unroll
-            for (int v = 0; v < kWaves; ++v) {
-                const float mv = ml[v * 16 + head];
-                if (mv == kNegInf) continue;
-                const float sc = exp2_fast(mv - M);
-                const float *src = merge_area(v);
-                L += ml[kWaves * 16 + v * 16 + head] * sc;
-                O += src[head * D + d] * sc;
+                for (int v = 0; v < kWaves; ++v) {
+                    const float mv = ml[v * 16 + head];
+                    if (mv == kNegInf) continue;
+                    const float sc = exp2_fast(mv - M);
+                    const float *src = merge_area(v);
+                    Ls += ml[kWaves * 16 + v * 16 + head] * sc;
+                    O += src[head * D + d] * sc;
+                }
             }
+            const size_t row = (((size_t)b * T + gcol / G) * a.Hq + hk * G + gcol % G) * a.splits + split;
+            float o_out = Ls > 0.f ? O / Ls * a.v_scale : 0.f;
+            float lse_out = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : kNegInf;
+            if (any_bad) {
+                o_out = __builtin_nanf("");
+                lse_out = __builtin_nanf("");
+            }
+            a.part_o[row * D + d] = o_out;
+            if (d == 0) a.part_lse[row] = lse_out;
         }
-        const size_t row = (((size_t)b * T + gcol / G) * a.Hq + hk * G + gcol % G) * a.splits + split;
-        float o_out = L > 0.f ? O / L * a.v_scale : 0.f;
-        float lse_out = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
-        if (any_bad) {
-            o_out = __builtin_nanf("");
-            lse_out = __builtin_nanf("");
-        }
-        a.part_o[row * D + d] = o_out;
-        if (d == 0) a.part_lse[row] = lse_out;
     }
 }
 
@@ -481,15 +526,31 @@ __global__ void __launch_bounds__(kThreads) decode_combine_kernel(DecodeArgs a)
     }
 }
 
+template <int D, int EB, int NCT>
+hipError_t launch_split(const DecodeArgs &a, long long n_ct, hipStream_t s)
+{
+    const long long units = (long long)a.B * a.Hkv * a.splits;
+    const long long g1 = (units + 7) / 8 * 8 * ((n_ct + NCT - 1) / NCT);
+    if (g1 <= 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_split_kernel<D, EB, NCT>), dim3((unsigned)g1), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+// Column tiles per workgroup: the fewest groups of at most max_tiles<D>()
+// tiles, the tiles spread evenly over them (the last group may run an empty
+// tile or two).
 template <int D, int EB>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
 {
-    const long long units = (long long)a.B * a.Hkv * a.splits;
     const long long n_ct = ((long long)(a.Hq / a.Hkv) * a.T + 15) / 16;
-    const long long g1 = (units + 7) / 8 * 8 * n_ct;
-    if (g1 <= 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_split_kernel<D, EB>), dim3((unsigned)g1), dim3(kThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
+    const long long n_grp = (n_ct + max_tiles<D>() - 1) / max_tiles<D>();
+    const long long nct = n_grp > 0 ? (n_ct + n_grp - 1) / n_grp : 1;
+    hipError_t e;
+    if (nct <= 1) e = launch_split<D, EB, 1>(a, n_ct, s);
+    else if (nct == 2) e = launch_split<D, EB, 2>(a, n_ct, s);
+    else if (nct == 3) e = launch_split<D, EB, 3>(a, n_ct, s);
+    else e = launch_split<D, EB, max_tiles<D>()>(a, n_ct, s);
+    if (n_ct <= 0 || (long long)a.B * a.Hkv * a.splits <= 0) return e;
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.B * a.T * a.Hq)), dim3(kThreads), 0, s, a);
     return hipGetLastError();

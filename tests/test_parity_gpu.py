@@ -481,6 +481,11 @@ def test_prefill_paged_long_chunk_sampled(afa):
     ([300, 1500], 4, 64, 8, 128, 8),            # G*T = 32: two column tiles
     ([77, 2049, 600], 5, 64, 8, 128, 6),        # G*T = 40: a partial third tile
     ([513, 31], 1, 64, 2, 128, 4),              # one token, G = 32
+    ([300, 1200], 8, 64, 8, 128, 4),            # 4 tiles: two workgroups of 2
+    ([1000, 45, 333], 10, 64, 8, 128, 5),       # 5 tiles: groups of 3, one empty tile
+    ([513, 2000], 16, 16, 1, 128, 6),           # 256 columns: 16 tiles, 6 groups of 3
+    ([257, 90], 7, 32, 4, 64, 2),               # D = 64, 4 tiles in one workgroup
+    ([400, 901], 13, 32, 2, 64, 3),             # D = 64, 13 tiles: 4 groups of 4, three empty
 ])
 def test_decode_multi_matches_oracle_and_chunked_prefill(afa, ctx, T, Hq, Hkv, D, splits):
     say(f"case decode_multi ctx{ctx} T{T} Hq{Hq} Hkv{Hkv} D{D} splits{splits}")
@@ -538,6 +543,8 @@ def fp8_oracle(inp, q, scale, seqs=None):
     ([300, 45], 1, 8, 2, 64, 3, 0.04, 0.04),                # D = 64
     ([300, 77, 1000], 4, 8, 2, 128, 4, 0.03, 0.03),        # 4 new tokens per sequence
     ([700, 90], 4, 64, 8, 128, 8, 0.03, 0.05),             # G*T = 32: two column tiles
+    ([700, 90], 6, 64, 8, 128, 8, 0.03, 0.05),             # three column tiles in one workgroup
+    ([300, 45], 8, 32, 4, 64, 3, 0.04, 0.02),              # D = 64, four column tiles
 ])
 def test_decode_fp8_matches_oracle(afa, ctx, T, Hq, Hkv, D, splits, ks, vs):
     from attention_flash_fwd_amd import inputs

@@ -109,8 +109,8 @@ def test_decode_random(afa, seed):
     nseq = int(rng.integers(1, 9))
     Hq, Hkv = heads(rng, max_hq=64)
     D = int(rng.choice([64, 128]))
-    T = int(rng.integers(1, 5))
-    while (Hq // Hkv) * T > 64:
+    T = int(rng.integers(1, 5)) if rng.random() < 0.5 else int(rng.integers(5, 17))
+    while (Hq // Hkv) * T > 256:
         T -= 1
     ctx = [int(rng.integers(1, 3000)) for _ in range(nseq)]
     splits = int(rng.choice([0, 1, 2, 3, 5, 8, 13, 32]))
