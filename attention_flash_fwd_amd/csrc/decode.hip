@@ -42,15 +42,20 @@ namespace {
 
 constexpr int kBS = 16;         // tokens per cache block
 constexpr int kWaves = 4;
-// 16-column tiles one split workgroup computes at most: as many as the
-// per-tile Q operands and accumulators (3 D / 8 + 2 registers a tile) leave
-// room for within 256 registers.
-template <int D>
-constexpr int max_tiles() { return D == 128 ? 3 : 4; }
+// 16-column tiles one split workgroup computes at most.  A tile holds its
+// accumulator (D / 8 registers), its row statistics and, in registers, its
+// Q operand (D / 16).  With D = 128, four tiles fit 256 registers only once
+// their Q operands move to LDS (16 KiB, which with the 64 KiB ring still
+// lets two workgroups share a CU).
+constexpr int kMaxTiles = 4;
+template <int D, int NCT>
+constexpr bool qs_in_lds() { return D == 128 && NCT == 4; }
 constexpr int kThreads = 64 * kWaves;
 constexpr uint32_t kOutside = 0x80000000u;   // buffer offset past any block: reads zero
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
 
 __device__ __forceinline__ f32x4_t mfma_16x16x16_bf16(u32x2_t a, u32x2_t b, f32x4_t c)
 {
@@ -143,10 +148,12 @@ __device__ __forceinline__ void convert_v(const uint8_t *vs, uint8_t *cv, int la
 // One block: scores, online softmax, PV, for NCT column tiles at once.  ks
 // holds K with EB-byte elements; vs holds V as bf16 (for fp8 caches, the
 // converted scratch copy).  Each K fragment and each V^T fragment read from
-// LDS feeds the products of every tile.
-template <int D, int EB, int NCT>
-__device__ __forceinline__ void compute_block(const uint8_t *ks, const uint8_t *vs, int valid,
-                                              bool causal, int tok0, const int (&lim)[NCT],
+// LDS feeds the products of every tile.  With QL the Q^T operands come from
+// LDS (qs: this lane's fragment of tile 0, kk 0; the fragments of (c, kk)
+// follow at a stride of 1 KiB) instead of w[c].qf.
+template <int D, int EB, int NCT, bool QL>
+__device__ __forceinline__ void compute_block(const uint8_t *ks, const uint8_t *vs, lds_u8 *qs,
+                                              int valid, bool causal, int tok0, const int (&lim)[NCT],
                                               float scale_log2, int l16, int g, WaveState<D> (&w)[NCT])
 {
     using Gm = Geom<D, 2>;
@@ -169,7 +176,14 @@ __device__ __forceinline__ void compute_block(const uint8_t *ks, const uint8_t *
                 kf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
             }
 #pragma unroll
-            for (int c = 0; c < NCT; ++c) s[c] = mfma_16x16x32_bf16(kf, w[c].qf[kk], s[c]);
+            for (int c = 0; c < NCT; ++c) {
+                u32x4_t qop;
+                if constexpr (QL)
+                    qop = *reinterpret_cast<lds_u32x4 *>(qs + 1024 * (c * (D / 32) + kk));
+                else
+                    qop = w[c].qf[kk];
+                s[c] = mfma_16x16x32_bf16(kf, qop, s[c]);
+            }
         }
     }
     // Lane (g, l16) holds tokens 4 g + v of head l16.  One branch covers the
@@ -241,8 +255,16 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     __shared__ __attribute__((aligned(1024))) uint8_t k_s1[kWaves][Gm::slot_bytes];
     __shared__ __attribute__((aligned(1024))) uint8_t v_s1[kWaves][Gm::slot_bytes];
     // fp8 caches: each wave's V block converted to bf16 (one block).
-    constexpr int kCv = EB == 1 ? Geom<D, 2>::slot_bytes : 16;
-    __shared__ __attribute__((aligned(1024))) uint8_t v_cv[kWaves][kCv];
+    // One more area after the ring: for fp8 caches, each wave's V block
+    // converted to bf16 (one block per wave); with QL, the Q^T operands of the
+    // NCT tiles, shared by the four waves (1 KiB per (tile, kk): 16 bytes a
+    // lane).  With neither, a token 16 bytes.
+    constexpr bool QL = qs_in_lds<D, NCT>();
+    constexpr int kCv = EB == 1 ? kWaves * Geom<D, 2>::slot_bytes : 0;
+    constexpr int kQs = QL ? NCT * (D / 32) * 1024 : 0;
+    __shared__ __attribute__((aligned(1024))) uint8_t aux[kCv + kQs > 0 ? kCv + kQs : 16];
+    uint8_t *const v_cv = aux;                          // [kWaves][block]
+    uint8_t *const q_s = aux + kCv;
 
     const int lane = threadIdx.x & 63;
     const int wave = (int)uniform_u32(threadIdx.x >> 6);
@@ -295,10 +317,16 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
         const bool hv = want < GT;
         const int col = min(want, GT - 1);
         const uint16_t *qp = a.q + (((size_t)b * T + col / G) * a.Hq + hk * G + col % G) * D + 8 * g;
+        if (!QL || c % kWaves == wave) {   // with QL, wave c % 4 stages tile c
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-            const u32x4_t x = *reinterpret_cast<const u32x4_t *>(qp + 32 * kk);
-            w[c].qf[kk] = hv ? x : u32x4_t{0, 0, 0, 0};
+            for (int kk = 0; kk < D / 32; ++kk) {
+                const u32x4_t x = *reinterpret_cast<const u32x4_t *>(qp + 32 * kk);
+                const u32x4_t v = hv ? x : u32x4_t{0, 0, 0, 0};
+                if constexpr (QL)
+                    *reinterpret_cast<u32x4_t *>(q_s + 1024 * (c * (D / 32) + kk) + 16 * lane) = v;
+                else
+                    w[c].qf[kk] = v;
+            }
         }
 #pragma unroll
         for (int db = 0; db < D / 16; ++db) w[c].o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -359,12 +387,17 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     auto run = [&](const uint8_t *ks, const uint8_t *vs, int j) __attribute__((always_inline)) {
         const uint8_t *vb = vs;
         if constexpr (EB == 1) {
-            convert_v<D>(vs, v_cv[wave], lane);
+            convert_v<D>(vs, v_cv + wave * Geom<D, 2>::slot_bytes, lane);
             __builtin_amdgcn_wave_barrier();
-            vb = v_cv[wave];
+            vb = v_cv + wave * Geom<D, 2>::slot_bytes;
         }
-        compute_block<D, EB, NCT>(ks, vb, valid_rows(j), causal_blk(j), tok0_of(j), lim, a.scale_log2, l16, g, w);
+        // An LDS address the compiler cannot see through, so that it reads
+        // the Q operands in every block instead of keeping them live.
+        lds_u8 *qb = (lds_u8 *)(q_s + 16 * lane);
+        if constexpr (QL) asm volatile("" : "+v"(qb));
+        compute_block<D, EB, NCT, QL>(ks, vb, qb, valid_rows(j), causal_blk(j), tok0_of(j), lim, a.scale_log2, l16, g, w);
     };
+    if constexpr (QL) __syncthreads();              // the staged Q operands are visible
     issue(0, k_s0[wave], v_s0[wave]);
     issue(1, k_s1[wave], v_s1[wave]);
     for (int j = 0; j < nmine; j += 2) {
@@ -386,7 +419,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     // past the chunk end fetch nothing but still write zeros) and passed the
     // barrier.
     __builtin_amdgcn_s_waitcnt(0);
-    const bool any_bad = __syncthreads_or(bad);
+    __syncthreads();
     // Wave w's partial O (16 columns x D fp32): bf16 caches put two waves in
     // each of k_s0 / v_s0, fp8 caches one wave in each of the four slots.
     auto merge_area = [&](int v) __attribute__((always_inline)) -> float * {
@@ -396,7 +429,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
             return reinterpret_cast<float *>(v == 0 ? &k_s0[0][0] : v == 1 ? &v_s0[0][0] : v == 2 ? &k_s1[0][0] : &v_s1[0][0]);
     };
     float *mo = merge_area(wave);
-    float *ml = reinterpret_cast<float *>(EB == 2 ? &k_s1[0][0] : &v_cv[0][0]);   // [wave][16] m, then l
+    float *ml = reinterpret_cast<float *>(EB == 2 ? &k_s1[0][0] : v_cv);   // [wave][16] m, then l
+    int *flags = reinterpret_cast<int *>(ml + 2 * kWaves * 16);            // [wave] a bad block id seen
+    {
+        const bool wbad = wave_any(bad);
+        if (lane == 0) flags[wave] = wbad ? 1 : 0;
+    }
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
         const int col0 = col_base + 16 * c;
@@ -411,6 +449,9 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
         for (int db = 0; db < D / 16; ++db)
             *reinterpret_cast<f32x4_t *>(mo + l16 * D + 16 * db + 4 * g) = w[c].o[db];
         __syncthreads();
+        bool any_bad = false;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) any_bad |= flags[v] != 0;
 
         for (int idx = threadIdx.x; idx < NC * D; idx += kThreads) {
             const int head = idx / D, d = idx % D;      // head = matrix-core column of this tile
@@ -536,20 +577,20 @@ hipError_t launch_split(const DecodeArgs &a, long long n_ct, hipStream_t s)
     return hipGetLastError();
 }
 
-// Column tiles per workgroup: the fewest groups of at most max_tiles<D>()
-// tiles, the tiles spread evenly over them (the last group may run an empty
-// tile or two).
+// Column tiles per workgroup: the fewest groups of at most kMaxTiles tiles,
+// the tiles spread evenly over them (the last group may run an empty tile or
+// two).
 template <int D, int EB>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
 {
     const long long n_ct = ((long long)(a.Hq / a.Hkv) * a.T + 15) / 16;
-    const long long n_grp = (n_ct + max_tiles<D>() - 1) / max_tiles<D>();
+    const long long n_grp = (n_ct + kMaxTiles - 1) / kMaxTiles;
     const long long nct = n_grp > 0 ? (n_ct + n_grp - 1) / n_grp : 1;
     hipError_t e;
     if (nct <= 1) e = launch_split<D, EB, 1>(a, n_ct, s);
     else if (nct == 2) e = launch_split<D, EB, 2>(a, n_ct, s);
     else if (nct == 3) e = launch_split<D, EB, 3>(a, n_ct, s);
-    else e = launch_split<D, EB, max_tiles<D>()>(a, n_ct, s);
+    else e = launch_split<D, EB, kMaxTiles>(a, n_ct, s);
     if (n_ct <= 0 || (long long)a.B * a.Hkv * a.splits <= 0) return e;
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.B * a.T * a.Hq)), dim3(kThreads), 0, s, a);

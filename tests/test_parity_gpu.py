@@ -481,9 +481,10 @@ def test_prefill_paged_long_chunk_sampled(afa):
     ([300, 1500], 4, 64, 8, 128, 8),            # G*T = 32: two column tiles
     ([77, 2049, 600], 5, 64, 8, 128, 6),        # G*T = 40: a partial third tile
     ([513, 31], 1, 64, 2, 128, 4),              # one token, G = 32
-    ([300, 1200], 8, 64, 8, 128, 4),            # 4 tiles: two workgroups of 2
+    ([300, 1200], 8, 64, 8, 128, 4),            # 4 tiles in one workgroup, Q operands in LDS
     ([1000, 45, 333], 10, 64, 8, 128, 5),       # 5 tiles: groups of 3, one empty tile
-    ([513, 2000], 16, 16, 1, 128, 6),           # 256 columns: 16 tiles, 6 groups of 3
+    ([64, 700], 14, 64, 8, 128, 2),             # 7 tiles: groups of 4 (Q in LDS), one empty tile
+    ([513, 2000], 16, 16, 1, 128, 6),           # 256 columns: 16 tiles, 4 groups of 4
     ([257, 90], 7, 32, 4, 64, 2),               # D = 64, 4 tiles in one workgroup
     ([400, 901], 13, 32, 2, 64, 3),             # D = 64, 13 tiles: 4 groups of 4, three empty
 ])
@@ -544,6 +545,7 @@ def fp8_oracle(inp, q, scale, seqs=None):
     ([300, 77, 1000], 4, 8, 2, 128, 4, 0.03, 0.03),        # 4 new tokens per sequence
     ([700, 90], 4, 64, 8, 128, 8, 0.03, 0.05),             # G*T = 32: two column tiles
     ([700, 90], 6, 64, 8, 128, 8, 0.03, 0.05),             # three column tiles in one workgroup
+    ([700, 90], 8, 64, 8, 128, 8, 0.04, 0.03),             # four tiles, Q operands in LDS
     ([300, 45], 8, 32, 4, 64, 3, 0.04, 0.02),              # D = 64, four column tiles
 ])
 def test_decode_fp8_matches_oracle(afa, ctx, T, Hq, Hkv, D, splits, ks, vs):
