@@ -48,11 +48,16 @@
 // wave w loads its 8 rows of block 4 j + w / 2, whose physical id comes
 // through the scalar cache one step ahead.
 //
-// Grid: one workgroup per (q-tile, query head, batch).  Workgroup ids are
-// mapped so that all query heads of one (batch, KV head) land on the same
-// XCD (ids go round-robin over the 8 XCDs), each XCD works through its
-// (batch, KV head) pairs one at a time, and within a pair the longest
-// causal q-tiles start first: the pair's K/V stays in that XCD's L2.
+// Work items: one per (q-tile, query head, batch).  Item ids are mapped so
+// that all query heads of one (batch, KV head) belong to the same XCD (ids
+// go round-robin over the 8 XCDs), each XCD works through its (batch, KV
+// head) pairs one at a time, and within a pair the longest causal q-tiles
+// come first: the pair's K/V stays in that XCD's L2.  The grid is
+// persistent: one workgroup per CU, each looping over items of its XCD, so
+// that a CU goes from one item to the next without waiting for a workgroup
+// to retire and another to be dispatched.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "gfx950.hpp"
@@ -121,7 +126,7 @@ __device__ __forceinline__ void map_workgroup(int L, const PrefillArgs &a, int n
 
 template <int D, bool CAUSAL, bool PAGED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
+prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int n_items)
 {
     using T = Tile<D>;
     // Distinct arrays per slot, so that the compiler's wait for a slot's
@@ -136,8 +141,21 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
     const int grp = wave >> 2;
     const int l32 = lane & 31, h = lane >> 5;
 
+    // Workgroup w stays on XCD w % 8 and takes that XCD's items (ids L with
+    // L % 8 == w % 8) in rounds of one item per workgroup, the direction
+    // alternating between rounds: with the heaviest causal q-tiles first,
+    // every workgroup then gets about the same number of tiles.  Only the
+    // last round can run out of items, so the first missing item ends the
+    // loop.
+    const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3, nk = gridDim.x >> 3;
+    const int per_xcd = (n_items + 7) >> 3;
+    for (int round = 0;; ++round) {
+    const int rr = round * nk + ((round & 1) ? nk - 1 - kx : kx);
+    const int item = rr * 8 + xcd;
+    if (rr >= per_xcd || item >= n_items) break;
+
     int b, hq, qt;
-    map_workgroup(blockIdx.x, a, n_qtiles, b, hq, qt);
+    map_workgroup(item, a, n_qtiles, b, hq, qt);
     const int G = a.Hq / a.Hkv, hk = hq / G;
     const int i0 = qt * kBR;
     const int q0 = i0 + wave * 32;      // first query row of this wave (uniform)
@@ -230,7 +248,7 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
     // the workgroup's tiles).
     auto block_rows = [&](int t) __attribute__((always_inline)) {
         const int lb = (kBC / kBS) * t + (wave >> 1);
-        return (t < n) & (lb < n_lblocks) ? min(kBS, Sk - kBS * lb) : 0;
+        return ((t < n) & (lb < n_lblocks)) ? min(kBS, Sk - kBS * lb) : 0;
     };
     // Physical id of this wave's block of tile t, read through the scalar
     // cache at an index clamped into the table row (the value only matters
@@ -549,15 +567,34 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles)
             a.lse[((size_t)b * a.Hq + hq) * a.Sq + my_q] =
                 (PAGED && bad) ? __builtin_nanf("") : (ltot > 0.f ? (m + __log2f(ltot)) * kLn2 : kNegInf);
     }
+    }   // items
+}
+
+// Compute units of the current device (cached per device).
+int compute_units()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
 }
 
 template <int D, bool CAUSAL, bool PAGED>
 hipError_t launch_one(const PrefillArgs &a, hipStream_t s)
 {
     const int n_qtiles = (a.Sq + kBR - 1) / kBR;
-    const long long grid = (long long)n_qtiles * a.Hq * a.B;
-    if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, PAGED>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, n_qtiles);
+    const long long items = (long long)n_qtiles * a.Hq * a.B;
+    if (items <= 0) return hipSuccess;
+    // One workgroup per CU (a workgroup fills a CU's registers), a multiple
+    // of 8 so that each workgroup keeps to the items of one XCD.
+    const long long grid = std::min<long long>((items + 7) / 8 * 8, std::max(8, compute_units() / 8 * 8));
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, PAGED>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
+                       n_qtiles, (int)items);
     return hipGetLastError();
 }
 
