@@ -82,7 +82,7 @@ struct Geom {
     }
 };
 
-// Per-wave state of the split kernel.
+// Per-wave state of the split kernel for one 16-column tile.
 template <int D>
 struct WaveState {
     u32x4_t qf[D / 32];         // Q^T operand: head l16, d = 32 kk + 8 g .. +8
@@ -111,10 +111,6 @@ __device__ __forceinline__ void issue_block(const void *kc, const void *vc, long
     }
 }
 
-// One block from a slot: scores, online softmax, PV.
-// Tokens 4 g + v of the block at or past `valid` are masked; with `causal`
-// set, so is every token past `lim` (absolute position) for this lane's
-// column (the causal limit of its query among several new tokens).
 // Four e4m3 values -> four bf16 (exact: every e4m3 value is a bf16 value).
 __device__ __forceinline__ u32x2_t fp8x4_to_bf16(uint32_t x)
 {
@@ -151,6 +147,9 @@ __device__ __forceinline__ void convert_v(const uint8_t *vs, uint8_t *cv, int la
 // LDS feeds the products of every tile.  With QL the Q^T operands come from
 // LDS (qs: this lane's fragment of tile 0, kk 0; the fragments of (c, kk)
 // follow at a stride of 1 KiB) instead of w[c].qf.
+// Tokens 4 g + v of the block at or past `valid` are masked; with `causal`
+// set, so is every token past lim[c] (absolute position) for this lane's
+// column of tile c (the causal limit of its query among several new tokens).
 template <int D, int EB, int NCT, bool QL>
 __device__ __forceinline__ void compute_block(const uint8_t *ks, const uint8_t *vs, lds_u8 *qs,
                                               int valid, bool causal, int tok0, const int (&lim)[NCT],

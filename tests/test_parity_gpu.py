@@ -92,6 +92,8 @@ PREFILL_BF16_CASES = [
     (1, 130, 70, 4, 2, 128, False),
     (1, 512, 512, 8, 8, 64, True),      # two full 256-row workgroups, D = 64
     (2, 5, 1000, 4, 2, 128, False),     # few queries, many keys: one busy wave per workgroup
+    (4, 520, 520, 32, 8, 64, True),     # 384 items: a second, partial round of the resident grid
+    (3, 520, 520, 36, 12, 64, False),   # 324 items, (batch, KV head) pairs not a multiple of 8
 ]
 
 
