@@ -452,33 +452,51 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) any_bad |= flags[v] != 0;
 
-        for (int idx = threadIdx.x; idx < NC * D; idx += kThreads) {
-            const int head = idx / D, d = idx % D;      // head = matrix-core column of this tile
-            const int gcol = col0 + head;
+        // Thread (column hh, d range dq): 16 threads per column, D / 16
+        // consecutive d each; the column's wave weights are computed once.
+        // Waves that saw no visible key have m = -inf, l = 0 and O = 0, and
+        // add exact zeros.
+        constexpr int DPT = D / 16;
+        static_assert(kThreads == 16 * 16, "one thread per (column, d range)");
+        const int hh = threadIdx.x >> 4, dq = threadIdx.x & 15;
+        if (hh < NC) {
             float M = kNegInf;
 #pragma unroll
-            for (int v = 0; v < kWaves; ++v) M = fmaxf(M, ml[v * 16 + head]);
-            float Ls = 0.f, O = 0.f;
-            if (M != kNegInf) {
+            for (int v = 0; v < kWaves; ++v) M = fmaxf(M, ml[v * 16 + hh]);
+            float sc[kWaves];
+            float Ls = 0.f;
 #pragma unroll
-                for (int v = 0; v < kWaves; ++v) {
-                    const float mv = ml[v * 16 + head];
-                    if (mv == kNegInf) continue;
-                    const float sc = exp2_fast(mv - M);
-                    const float *src = merge_area(v);
-                    Ls += ml[kWaves * 16 + v * 16 + head] * sc;
-                    O += src[head * D + d] * sc;
+            for (int v = 0; v < kWaves; ++v) {
+                const float mv = ml[v * 16 + hh];
+                sc[v] = mv == kNegInf ? 0.f : exp2_fast(mv - M);
+                Ls += ml[kWaves * 16 + v * 16 + hh] * sc[v];
+            }
+            float o[DPT];
+#pragma unroll
+            for (int i = 0; i < DPT; ++i) o[i] = 0.f;
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v) {
+                const float *src = merge_area(v) + hh * D + dq * DPT;
+#pragma unroll
+                for (int i = 0; i < DPT; i += 4) {
+                    const f32x4_t x = *reinterpret_cast<const f32x4_t *>(src + i);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[i + e] += x[e] * sc[v];
                 }
             }
+            const int gcol = col0 + hh;
             const size_t row = (((size_t)b * T + gcol / G) * a.Hq + hk * G + gcol % G) * a.splits + split;
-            float o_out = Ls > 0.f ? O / Ls * a.v_scale : 0.f;
-            float lse_out = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : kNegInf;
-            if (any_bad) {
-                o_out = __builtin_nanf("");
-                lse_out = __builtin_nanf("");
+            float *dst = a.part_o + row * D + dq * DPT;
+#pragma unroll
+            for (int i = 0; i < DPT; i += 4) {
+                f32x4_t y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = Ls > 0.f ? o[i + e] / Ls * a.v_scale : 0.f;
+                if (any_bad) y = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+                *reinterpret_cast<f32x4_t *>(dst + i) = y;
             }
-            a.part_o[row * D + d] = o_out;
-            if (d == 0) a.part_lse[row] = lse_out;
+            if (dq == 0)
+                a.part_lse[row] = any_bad ? __builtin_nanf("") : (Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : kNegInf);
         }
     }
 }
