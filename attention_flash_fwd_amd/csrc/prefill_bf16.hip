@@ -549,24 +549,52 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int n_items)
     // ---- epilogue ----------------------------------------------------------
     if constexpr (PAGED) bad = __syncthreads_or(bad);
     const float ltot = pair_sum_halves(lsum);
-    if (my_q < a.Sq) {
+    {
+        // O rows through LDS, so that the stores write whole rows: each wave
+        // puts its 32 rows (bf16, 16-byte chunks XOR-swizzled by row) in its
+        // own 32 x D slice of the idle K/V ring (free since the last step's
+        // barrier), then 16 lanes (D = 128) or 8 (D = 64) store one row.
+        // Rows past the queries fall outside the store descriptor.
+        constexpr int CPR = D / 8;                  // 16-byte chunks per row
         float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
         if (PAGED && bad) inv = __builtin_nanf("");
-        uint16_t *op = static_cast<uint16_t *>(a.o) + (((size_t)b * a.Sq + my_q) * a.Hq + hq) * D;
+        uint16_t *stage = (wave < 2 ? k_s0 : wave < 4 ? k_s1 : wave < 6 ? v_s0 : v_s1) + (wave & 1) * 32 * D;
+        // Lane index through opaque(): the addresses below are then formed
+        // here, not hoisted out of the item loop into registers held
+        // across the main loop.
+        const int ln = opaque(lane), r32 = ln & 31, hh = ln >> 5;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                const int d0 = 32 * db + 8 * g4 + 4 * h;
+                // d = 32 db + 8 g4 + 4 h .. +3: half h of chunk 4 db + g4 of row l32
                 const u32x2_t w = {pack_bf16x2(oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv),
                                    pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
-                *reinterpret_cast<u32x2_t *>(op + d0) = w;
+                const int c = (4 * db + g4) ^ (r32 % CPR);
+                *reinterpret_cast<u32x2_t *>(stage + r32 * D + 8 * c + 4 * hh) = w;
             }
         }
+        const int rows = max(0, min(32, a.Sq - q0));
+        const uint32_t rstride = (uint32_t)(a.Hq * D * 2);
+        const __amdgpu_buffer_rsrc_t ro =
+            make_rsrc(static_cast<uint16_t *>(a.o) + (((size_t)b * a.Sq + q0) * a.Hq + hq) * D,
+                      rows > 0 ? (uint32_t)(rows - 1) * rstride + D * 2 : 0u);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 32 * CPR / 64; ++i) {
+            const int r = i * (64 / CPR) + ln / CPR, c = ln % CPR;
+            const u32x4_t x = *reinterpret_cast<const u32x4_t *>(stage + r * D + 8 * (c ^ (r % CPR)));
+            __builtin_amdgcn_raw_buffer_store_b128(x, ro, (uint32_t)r * rstride + 16u * c, 0, 0);
+        }
+    }
+    if (my_q < a.Sq) {
         if (a.lse != nullptr && h == 0)
             a.lse[((size_t)b * a.Hq + hq) * a.Sq + my_q] =
                 (PAGED && bad) ? __builtin_nanf("") : (ltot > 0.f ? (m + __log2f(ltot)) * kLn2 : kNegInf);
     }
+    // Every wave is done with its slice of the ring before the next item's
+    // K tile 0 lands there (the output stores may still be in flight).
+    lds_barrier();
     }   // items
 }
 
