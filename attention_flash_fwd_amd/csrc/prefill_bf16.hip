@@ -10,8 +10,12 @@
 // K/V blocks pipelined, row-max / row-sum reductions; its note on the cost
 // of warp specialisation motivates the two wave groups below):
 //
-//   one workgroup = 256 query rows of one (batch, query head): 8 waves of 32
-//   rows, one workgroup per CU.  Waves w and w + 4 share a SIMD; waves 0-3
+//   one work item = 256 query rows sharing one K/V stream: 256 rows of one
+//   (batch, query head), or, with causal masking and an even number of
+//   query heads per KV head, 128 rows of two such heads.  One workgroup per
+//   CU, 8 waves of 32 rows, takes items one after another and stages its
+//   output rows through LDS so that they are stored as whole rows.
+//   Waves w and w + 4 share a SIMD; waves 0-3
 //   (group 0) and 4-7 (group 1) run half a step apart, so that while one
 //   wave of a SIMD works on the matrix cores the other mostly works on the
 //   vector ALU.  K/V tiles of 64 keys stream through LDS (two slots each for
@@ -95,10 +99,12 @@ struct Tile {
     }
 };
 
-__device__ __forceinline__ void map_workgroup(int L, const PrefillArgs &a, int n_qtiles,
+// Item L -> (batch b, first query head hq, q-tile qt); an item covers hpi
+// consecutive query heads of one KV group.
+__device__ __forceinline__ void map_workgroup(int L, const PrefillArgs &a, int n_qtiles, int hpi,
                                               int &b, int &hq, int &qt)
 {
-    const int G = a.Hq / a.Hkv;
+    const int G = a.Hq / a.Hkv / hpi;               // items per (q-tile, KV head)
     const int groups = a.B * a.Hkv;                 // (batch, KV head) pairs
     int qt_rev, g, hg;
     if (groups % 8 == 0) {
@@ -120,14 +126,20 @@ __device__ __forceinline__ void map_workgroup(int L, const PrefillArgs &a, int n
         hg = rem % G;
     }
     b = g / a.Hkv;
-    hq = (g % a.Hkv) * G + hg;
+    hq = ((g % a.Hkv) * G + hg) * hpi;
     qt = n_qtiles - 1 - qt_rev;
 }
 
-template <int D, bool CAUSAL, bool PAGED>
+// PAIR: an item is 128 rows of two query heads of one KV group instead of
+// 256 rows of one head.  The K/V tiles still serve 256 rows, but the causal
+// diagonal crosses two tiles instead of four, so fewer waves sit idle while
+// the others finish their diagonal tiles.
+template <int D, bool CAUSAL, bool PAGED, bool PAIR>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int n_items)
 {
+    constexpr int RPH = PAIR ? kBR / 2 : kBR;       // rows per head of an item
+    constexpr int HPI = PAIR ? 2 : 1;               // query heads per item
     using T = Tile<D>;
     // Distinct arrays per slot, so that the compiler's wait for a slot's
     // LDS-direct loads never covers the loads in flight to the other slot.
@@ -154,11 +166,17 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int n_items)
     const int item = rr * 8 + xcd;
     if (rr >= per_xcd || item >= n_items) break;
 
-    int b, hq, qt;
-    map_workgroup(item, a, n_qtiles, b, hq, qt);
-    const int G = a.Hq / a.Hkv, hk = hq / G;
-    const int i0 = qt * kBR;
-    const int q0 = i0 + wave * 32;      // first query row of this wave (uniform)
+    int b, hq0, qt;
+    map_workgroup(item, a, n_qtiles, HPI, b, hq0, qt);
+    const int G = a.Hq / a.Hkv, hk = hq0 / G;
+    // This wave's head and 32-row block.  With PAIR, waves 0-3 take rows
+    // 0..127 of head hq0 and waves 4-7 rows 127..0 of head hq0 + 1, so the
+    // two waves of a SIMD (w and w + 4) reach the diagonal at different
+    // tiles.
+    const int hq = hq0 + (PAIR ? (wave >> 2) : 0);
+    const int rb = PAIR ? ((wave < 4) ? wave : 7 - wave) : wave;
+    const int i0 = qt * RPH;
+    const int q0 = i0 + rb * 32;        // first query row of this wave (uniform)
     const int my_q = q0 + l32;          // query row of this lane
     // Keys of this sequence.  Paged: read through the scalar cache (so that
     // everything derived from it stays wave-uniform); a length outside the
@@ -175,7 +193,7 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int n_items)
     const int diag = Sk - a.Sq;         // key j visible to row i iff j <= i + diag
 
     int kend = Sk;                      // keys [0, kend) may be visible to this workgroup
-    if (CAUSAL) kend = min(Sk, min(a.Sq, i0 + kBR) + diag);
+    if (CAUSAL) kend = min(Sk, min(a.Sq, i0 + RPH) + diag);
     const int n = kend > 0 ? (kend + kBC - 1) / kBC : 0;
     // Tiles [0, nw) hold keys visible to some row of this wave; from step nw
     // on the wave only issues its share of the loads (its P would be 0).
@@ -612,18 +630,27 @@ int compute_units()
     return v;
 }
 
-template <int D, bool CAUSAL, bool PAGED>
-hipError_t launch_one(const PrefillArgs &a, hipStream_t s)
+template <int D, bool CAUSAL, bool PAGED, bool PAIR>
+hipError_t launch_items(const PrefillArgs &a, hipStream_t s)
 {
-    const int n_qtiles = (a.Sq + kBR - 1) / kBR;
-    const long long items = (long long)n_qtiles * a.Hq * a.B;
+    constexpr int RPH = PAIR ? kBR / 2 : kBR;
+    const int n_qtiles = (a.Sq + RPH - 1) / RPH;
+    const long long items = (long long)n_qtiles * (a.Hq / (PAIR ? 2 : 1)) * a.B;
     if (items <= 0) return hipSuccess;
     // One workgroup per CU (a workgroup fills a CU's registers), a multiple
     // of 8 so that each workgroup keeps to the items of one XCD.
     const long long grid = std::min<long long>((items + 7) / 8 * 8, std::max(8, compute_units() / 8 * 8));
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, PAGED>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, PAGED, PAIR>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
                        n_qtiles, (int)items);
     return hipGetLastError();
+}
+
+// Causal with an even number of query heads per KV head: items of two heads.
+template <int D, bool CAUSAL, bool PAGED>
+hipError_t launch_one(const PrefillArgs &a, hipStream_t s)
+{
+    if (CAUSAL && (a.Hq / a.Hkv) % 2 == 0) return launch_items<D, CAUSAL, PAGED, CAUSAL>(a, s);
+    return launch_items<D, CAUSAL, PAGED, false>(a, s);
 }
 
 }  // namespace
