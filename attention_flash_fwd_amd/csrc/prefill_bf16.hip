@@ -11,8 +11,8 @@
 // of warp specialisation motivates the two wave groups below):
 //
 //   one work item = 256 query rows sharing one K/V stream: 256 rows of one
-//   (batch, query head), or, with causal masking and an even number of
-//   query heads per KV head, 128 rows of two such heads.  One workgroup per
+//   (batch, query head), or, with causal masking, 128 rows of two or 64 rows
+//   of four query heads of the same KV head (as the group size allows).  One workgroup per
 //   CU, 8 waves of 32 rows, takes items one after another and stages its
 //   output rows through LDS so that they are stored as whole rows.
 //   Waves w and w + 4 share a SIMD; waves 0-3
@@ -130,16 +130,16 @@ __device__ __forceinline__ void map_workgroup(int L, const PrefillArgs &a, int n
     qt = n_qtiles - 1 - qt_rev;
 }
 
-// PAIR: an item is 128 rows of two query heads of one KV group instead of
-// 256 rows of one head.  The K/V tiles still serve 256 rows, but the causal
-// diagonal crosses two tiles instead of four, so fewer waves sit idle while
-// the others finish their diagonal tiles.
-template <int D, bool CAUSAL, bool PAGED, bool PAIR>
+// HPI query heads of one KV group per item, 256 / HPI rows each.  The K/V
+// tiles still serve 256 rows, but the causal diagonal of an item crosses
+// 4 / HPI tiles, so fewer waves sit idle while the others finish their
+// diagonal tiles (with HPI = 4, none).
+template <int D, bool CAUSAL, bool PAGED, int HPI>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int n_items)
 {
-    constexpr int RPH = PAIR ? kBR / 2 : kBR;       // rows per head of an item
-    constexpr int HPI = PAIR ? 2 : 1;               // query heads per item
+    static_assert(HPI == 1 || HPI == 2 || HPI == 4, "heads per item");
+    constexpr int RPH = kBR / HPI;                  // rows per head of an item
     using T = Tile<D>;
     // Distinct arrays per slot, so that the compiler's wait for a slot's
     // LDS-direct loads never covers the loads in flight to the other slot.
@@ -169,12 +169,12 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int n_items)
     int b, hq0, qt;
     map_workgroup(item, a, n_qtiles, HPI, b, hq0, qt);
     const int G = a.Hq / a.Hkv, hk = hq0 / G;
-    // This wave's head and 32-row block.  With PAIR, waves 0-3 take rows
+    // This wave's head and 32-row block.  HPI = 2: waves 0-3 take rows
     // 0..127 of head hq0 and waves 4-7 rows 127..0 of head hq0 + 1, so the
     // two waves of a SIMD (w and w + 4) reach the diagonal at different
-    // tiles.
-    const int hq = hq0 + (PAIR ? (wave >> 2) : 0);
-    const int rb = PAIR ? ((wave < 4) ? wave : 7 - wave) : wave;
+    // tiles.  HPI = 4: waves 2j and 2j + 1 take rows 0..63 of head hq0 + j.
+    const int hq = hq0 + (HPI == 4 ? (wave >> 1) : HPI == 2 ? (wave >> 2) : 0);
+    const int rb = HPI == 4 ? (wave & 1) : HPI == 2 ? ((wave < 4) ? wave : 7 - wave) : wave;
     const int i0 = qt * RPH;
     const int q0 = i0 + rb * 32;        // first query row of this wave (uniform)
     const int my_q = q0 + l32;          // query row of this lane
@@ -630,27 +630,32 @@ int compute_units()
     return v;
 }
 
-template <int D, bool CAUSAL, bool PAGED, bool PAIR>
+template <int D, bool CAUSAL, bool PAGED, int HPI>
 hipError_t launch_items(const PrefillArgs &a, hipStream_t s)
 {
-    constexpr int RPH = PAIR ? kBR / 2 : kBR;
+    constexpr int RPH = kBR / HPI;
     const int n_qtiles = (a.Sq + RPH - 1) / RPH;
-    const long long items = (long long)n_qtiles * (a.Hq / (PAIR ? 2 : 1)) * a.B;
+    const long long items = (long long)n_qtiles * (a.Hq / HPI) * a.B;
     if (items <= 0) return hipSuccess;
     // One workgroup per CU (a workgroup fills a CU's registers), a multiple
     // of 8 so that each workgroup keeps to the items of one XCD.
     const long long grid = std::min<long long>((items + 7) / 8 * 8, std::max(8, compute_units() / 8 * 8));
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, PAGED, PAIR>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, PAGED, HPI>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
                        n_qtiles, (int)items);
     return hipGetLastError();
 }
 
-// Causal with an even number of query heads per KV head: items of two heads.
+// Causal: as many query heads per item (4, 2 or 1) as divide the heads per
+// KV head.
 template <int D, bool CAUSAL, bool PAGED>
 hipError_t launch_one(const PrefillArgs &a, hipStream_t s)
 {
-    if (CAUSAL && (a.Hq / a.Hkv) % 2 == 0) return launch_items<D, CAUSAL, PAGED, CAUSAL>(a, s);
-    return launch_items<D, CAUSAL, PAGED, false>(a, s);
+    const int G = a.Hq / a.Hkv;
+    if constexpr (CAUSAL) {
+        if (G % 4 == 0) return launch_items<D, CAUSAL, PAGED, 4>(a, s);
+        if (G % 2 == 0) return launch_items<D, CAUSAL, PAGED, 2>(a, s);
+    }
+    return launch_items<D, CAUSAL, PAGED, 1>(a, s);
 }
 
 }  // namespace

@@ -345,7 +345,7 @@ def main():
     if pf_in is not None:
         digest = source_digest(KERNEL_SOURCES["prefill"])
         achieved = out_parts["prefill"]["tflops"]
-        roofline = {"bound": "mfma", "kernel": "prefill_bf16_kernel<128, true, false, true>",
+        roofline = {"bound": "mfma", "kernel": "prefill_bf16_kernel<128, true, false, 4>",
                     "achieved": achieved, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                     "frac": achieved * 1e12 / PEAK_BF16_FLOPS, "traffic": load_traffic("prefill", digest),
                     "per_launch_flops": pf_cfg.flops(), "avg_launch_ms": part_ms["prefill"],
