@@ -94,6 +94,8 @@ PREFILL_BF16_CASES = [
     (2, 5, 1000, 4, 2, 128, False),     # few queries, many keys: one busy wave per workgroup
     (4, 520, 520, 32, 8, 64, True),     # 384 items: a second, partial round of the resident grid
     (3, 520, 520, 36, 12, 64, False),   # 324 items, (batch, KV head) pairs not a multiple of 8
+    (2, 300, 300, 9, 3, 128, True),     # causal, group size 3: one query head per item
+    (1, 400, 400, 12, 2, 64, True),     # causal, group size 6: two query heads per item
 ]
 
 

@@ -37,9 +37,11 @@ def afa(cuda):
 
 
 def heads(rng, max_hq=32):
+    # Group sizes that are odd, even but not a multiple of 4, and multiples
+    # of 4 (the prefill kernel takes 1, 2 or 4 query heads per work item).
     while True:
-        hkv = int(rng.choice([1, 2, 4, 8]))
-        g = int(rng.choice([1, 2, 4, 8, 16]))
+        hkv = int(rng.choice([1, 2, 3, 4, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16]))
         if hkv * g <= max_hq:
             return hkv * g, hkv
 
