@@ -1,10 +1,11 @@
-// decode.hip -- single-token attention over a paged KV cache, Flash-Decoding
-// style ("GPU Kernel 调度：大模型推理的拐点 2026", paragraphs on Flash Decoding
-// and its cost: the cached K/V of a sequence is cut into chunks processed in
-// parallel, each chunk yields a partial output with its log-sum-exp, and a
-// small reduce kernel merges the partials with the online-softmax formula in
-// fp32; chenyy20.com "抱infra脚", section Paged Attention: fixed-size blocks
-// reached through a block table).
+// decode.hip -- attention of one (or a few) new tokens per sequence over a
+// paged KV cache, Flash-Decoding style ("GPU Kernel 调度：大模型推理的拐点
+// 2026", paragraphs on Flash Decoding and its cost: the cached K/V of a
+// sequence is cut into chunks processed in parallel, each chunk yields a
+// partial output with its log-sum-exp, and a small reduce kernel merges the
+// partials with the online-softmax formula in fp32; chenyy20.com
+// "抱infra脚", section Paged Attention: fixed-size blocks reached through a
+// block table).
 //
 // Kernel 1, decode_split: one workgroup of four waves per (chunk, KV head,
 //   sequence).  The G = Hq / Hkv query heads that share the KV head, times
@@ -253,7 +254,6 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     __shared__ __attribute__((aligned(1024))) uint8_t v_s0[kWaves][Gm::slot_bytes];
     __shared__ __attribute__((aligned(1024))) uint8_t k_s1[kWaves][Gm::slot_bytes];
     __shared__ __attribute__((aligned(1024))) uint8_t v_s1[kWaves][Gm::slot_bytes];
-    // fp8 caches: each wave's V block converted to bf16 (one block).
     // One more area after the ring: for fp8 caches, each wave's V block
     // converted to bf16 (one block per wave); with QL, the Q^T operands of the
     // NCT tiles, shared by the four waves (1 KiB per (tile, kk): 16 bytes a

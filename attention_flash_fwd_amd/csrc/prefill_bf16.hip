@@ -11,11 +11,11 @@
 // of warp specialisation motivates the two wave groups below):
 //
 //   one work item = 256 query rows sharing one K/V stream: 256 rows of one
-//   (batch, query head), or, with causal masking, 128 rows of two or 64 rows
-//   of four query heads of the same KV head (as the group size allows).  One workgroup per
-//   CU, 8 waves of 32 rows, takes items one after another and stages its
-//   output rows through LDS so that they are stored as whole rows.
-//   Waves w and w + 4 share a SIMD; waves 0-3
+//   (batch, query head), or, with causal masking, 128 rows of two or 64
+//   rows of four query heads of the same KV head (as the group size
+//   allows).  One workgroup per CU, 8 waves of 32 rows, takes items one
+//   after another and stages its output rows through LDS so that they are
+//   stored as whole rows.  Waves w and w + 4 share a SIMD; waves 0-3
 //   (group 0) and 4-7 (group 1) run half a step apart, so that while one
 //   wave of a SIMD works on the matrix cores the other mostly works on the
 //   vector ALU.  K/V tiles of 64 keys stream through LDS (two slots each for
@@ -39,7 +39,7 @@
 //     every wave issues its share of the loads of K(s+1) and V(s), which land
 //     by the step's closing barrier.
 //   A wave computes the tiles up to its own last visible key; for the
-//   remaining steps of its workgroup (past its diagonal) it only issues its
+//   remaining steps of its item (past its diagonal) it only issues its
 //   share of the loads.  These are separate loops, so no branch inside a
 //   step ever touches the output accumulators.
 //   Epilogue: O = O / l rounded to bf16, lse = (m + log2 l) * ln 2.
@@ -70,7 +70,7 @@
 namespace attn {
 namespace {
 
-constexpr int kBR = 256;      // query rows per workgroup
+constexpr int kBR = 256;      // query rows per work item (all heads of the item together)
 constexpr int kBC = 64;       // keys per K/V tile
 constexpr int kBS = 16;       // tokens per cache block (paged keys and values)
 constexpr int kThreads = 512;
@@ -112,7 +112,7 @@ __device__ __forceinline__ void map_workgroup(int L, const PrefillArgs &a, int n
         // group-major on each XCD: all q-tiles of one (batch, KV head) pair,
         // heaviest first, before the next pair, so that one pair's K/V is
         // the XCD's L2 working set
-        const int per = n_qtiles * G;               // workgroups of one pair
+        const int per = n_qtiles * G;               // items of one pair
         const int gi = r / per;
         const int rem = r - gi * per;
         qt_rev = rem / G;
@@ -192,7 +192,7 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int n_items)
     }
     const int diag = Sk - a.Sq;         // key j visible to row i iff j <= i + diag
 
-    int kend = Sk;                      // keys [0, kend) may be visible to this workgroup
+    int kend = Sk;                      // keys [0, kend) may be visible to this item
     if (CAUSAL) kend = min(Sk, min(a.Sq, i0 + RPH) + diag);
     const int n = kend > 0 ? (kend + kBC - 1) / kBC : 0;
     // Tiles [0, nw) hold keys visible to some row of this wave; from step nw
