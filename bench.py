@@ -196,7 +196,7 @@ def main():
         mcfg = inputs.DECODE_B64
         minp = inputs.decode_config_inputs(mcfg, device=dev)
         mq = inputs.chunk_queries(mcfg.batch, MULTI_T, mcfg.n_q_heads, mcfg.head_dim, seed=mcfg.seed, device=dev)
-        mws = afa.decode_workspace(mq, minp.k_cache, minp.block_table, mcfg.num_splits)
+        mws = afa.decode_workspace(mq, minp.k_cache, minp.block_table, 0)     # the library's split count
         mo = torch.empty_like(mq)
         mlse = torch.empty((mcfg.batch, mcfg.n_q_heads, MULTI_T), dtype=torch.float32, device=dev)
         extra_in["decode_multi"] = (mcfg, minp, mq, mws, mo, mlse)
@@ -241,7 +241,7 @@ def main():
     def run_multi():
         mcfg, minp, mq, mws, mo, mlse = extra_in["decode_multi"]
         afa.decode_paged_multi(mq, minp.k_cache, minp.v_cache, minp.block_table, minp.ctx_lens,
-                               num_splits=mcfg.num_splits, scale=mcfg.scale, out=mo, lse_out=mlse,
+                               num_splits=0, scale=mcfg.scale, out=mo, lse_out=mlse,
                                workspace=mws)
 
     def run_fp8():
@@ -314,12 +314,15 @@ def main():
                             "frac_of_peak": gbps * 1e9 / PEAK_HBM_BPS, "bytes": nb,
                             "num_splits": fcfg.num_splits, "kv_format": "e4m3, per-tensor scale"}
         elif name == "decode_multi":
-            mcfg, minp, mq = extra_in[name][:3]
+            mcfg, minp, mq, mws = extra_in[name][:4]
             nb = decode_bytes(minp, mcfg.n_q_heads) + 2 * (MULTI_T - 1) * mq[:, 0].numel() * 2
             gbps = nb / (ms * 1e-3) / 1e9
+            # the library's split count, read back from its workspace size (fp32 partial
+            # outputs and log-sum-exps per (sequence, token, query head, split), 256-byte aligned)
+            splits = mws.numel() // (mq.shape[0] * mq.shape[1] * mq.shape[2] * (mq.shape[3] + 1) * 4)
             extras[name] = {"workload": f"{mcfg.name}_T{MULTI_T}", "ms": ms, "gbps": gbps,
                             "frac_of_peak": gbps * 1e9 / PEAK_HBM_BPS, "bytes": nb,
-                            "num_splits": mcfg.num_splits}
+                            "num_splits": int(splits)}
     out_parts = {}
     sol_ms = 0.0
     if pf_in is not None:

@@ -239,6 +239,14 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
  * arguments).  A token with no visible key gets O = 0, lse = -inf.
  * Supported: (n_q_heads / n_kv_heads) * seqlen_q <= 256, plus the limits of
  * attn_decode_paged; seqlen_q == 1 is attn_decode_paged.
+ *
+ * num_splits <= 0 with seqlen_q > 1: the library's choice, again from the
+ * arguments alone.  Each chunk writes a partial output per (token, query
+ * head), so with C = (n_q_heads / n_kv_heads) * seqlen_q the chunks are
+ * about 2048 * min(4, max(1, C / 4)) tokens of the longest sequence the
+ * table can hold.  More chunks (none shorter than 256 tokens) are used only
+ * until about 512 workgroups occupy the GPU.  attn_decode_multi_workspace_bytes
+ * sizes the workspace for the same choice.
  */
 attn_status_t attn_decode_paged_multi(const void *q, const void *k_cache, const void *v_cache,
                                       const int32_t *block_table, const int32_t *ctx_lens,
@@ -283,8 +291,10 @@ attn_status_t attn_decode_paged_fp8(const void *q, const void *k_cache, const vo
 /*
  * attn_decode_multi_workspace_bytes -- workspace of attn_decode_paged_multi:
  * partial outputs [batch, seqlen_q, n_q_heads, splits, head_dim] fp32, then
- * their log-sum-exps [batch, seqlen_q, n_q_heads, splits] fp32.  Returns 0
- * for invalid arguments.
+ * their log-sum-exps [batch, seqlen_q, n_q_heads, splits] fp32, with splits
+ * the count attn_decode_paged_multi uses for these arguments
+ * (attn_decode_num_splits when seqlen_q == 1).  Returns 0 for invalid
+ * arguments.
  */
 size_t attn_decode_multi_workspace_bytes(int batch, int seqlen_q, int n_q_heads, int n_kv_heads,
                                          int head_dim, int max_blocks_per_seq, int block_size,
@@ -296,7 +306,7 @@ const char *attn_status_string(attn_status_t status);
 /* ABI version of this header: (major << 16) | minor. */
 int attn_abi_version(void);
 
-#define ATTN_ABI_VERSION ((1 << 16) | 3)
+#define ATTN_ABI_VERSION ((1 << 16) | 4)
 
 #ifdef __cplusplus
 }

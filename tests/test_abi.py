@@ -59,7 +59,7 @@ def test_exports_are_c_symbols():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.attn_abi_version() == (1 << 16) | 3
+    assert lib.attn_abi_version() == (1 << 16) | 4
     for code in range(8):
         s = lib.attn_status_string(code).decode()
         assert s and s != "unknown status"
@@ -215,6 +215,34 @@ def test_workspace_and_split_rules(lib):
             assert B * Hkv * s >= 1024
     assert lib.attn_decode_num_splits(-1, 8, 4, 16, 0) == 0
     assert lib.attn_decode_workspace_bytes(1, 0, 1, 128, 4, 16, 1) == 0
+
+
+def multi_splits(lib, B, T, Hq, Hkv, D, mb, S):
+    """Split count of attn_decode_paged_multi, read back from its workspace size."""
+    nbytes = lib.attn_decode_multi_workspace_bytes(B, T, Hq, Hkv, D, mb, 16, S)
+    per_split = B * T * Hq * (D + 1) * 4
+    s = nbytes // per_split
+    assert s * per_split <= nbytes < (s + 1) * per_split   # only the 256-byte alignment on top
+    return s
+
+
+def test_multi_token_split_rule(lib):
+    # One token: the single-token rule; explicit counts pass through.
+    for B, Hq, Hkv, mb in [(64, 32, 8, 2048), (4, 64, 8, 8192)]:
+        assert multi_splits(lib, B, 1, Hq, Hkv, 128, mb, 0) == lib.attn_decode_num_splits(B, Hkv, mb, 16, 0)
+        assert multi_splits(lib, B, 4, Hq, Hkv, 128, mb, 7) == 7
+    # Several tokens: chunks of 2048 * min(4, max(1, C / 4)) tokens of the
+    # longest sequence, C = G * T columns, or more chunks up to about 512
+    # workgroups (column-tile groups of 4 x 16 columns each count).
+    assert multi_splits(lib, 64, 2, 32, 8, 128, 2048, 0) == 8      # C = 8:  chunks of 4096 tokens
+    assert multi_splits(lib, 64, 4, 32, 8, 128, 2048, 0) == 4      # C = 16: chunks of 8192 tokens
+    assert multi_splits(lib, 64, 8, 32, 8, 128, 2048, 0) == 4      # C = 32: capped at 4 x 2048
+    assert multi_splits(lib, 4, 8, 64, 8, 128, 8192, 0) == 16      # 32 (seq, KV head) pairs: 512 / 32
+    assert multi_splits(lib, 1, 2, 8, 8, 64, 4, 0) == 1            # 64 tokens: one chunk of at least 256
+    for B, T, Hq, Hkv, mb in [(1, 3, 4, 1, 1), (2, 16, 16, 1, 300), (8, 5, 64, 8, 9000)]:
+        s = multi_splits(lib, B, T, Hq, Hkv, 64, mb, 0)
+        assert 1 <= s <= 256
+        assert s <= max(1, (mb * 16 + 255) // 256)
 
 
 def test_binding_rejects_cpu_tensors():
