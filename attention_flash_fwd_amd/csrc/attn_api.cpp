@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -94,8 +95,27 @@ int resolve_splits_multi(int batch, int seqlen_q, int n_q_heads, int n_kv_heads,
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 size_t part_o_bytes(int B, int Hq, int D, int S) { return align_up((size_t)B * Hq * S * D * sizeof(float), 256); }
+size_t part_lse_bytes(int B, int Hq, int S) { return align_up((size_t)B * Hq * S * sizeof(float), 256); }
+constexpr size_t kSchedBytes = 256;     // the split kernel's work counter, after the partials
 
 }  // namespace
+
+namespace attn {
+
+int compute_units()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+}  // namespace attn
 
 extern "C" {
 
@@ -206,8 +226,7 @@ size_t attn_decode_multi_workspace_bytes(int batch, int seqlen_q, int n_q_heads,
                                        num_splits);
     if (S <= 0) return 0;
     const int rows = batch * seqlen_q;
-    return part_o_bytes(rows, n_q_heads, head_dim, S) +
-           align_up((size_t)rows * n_q_heads * S * sizeof(float), 256);
+    return part_o_bytes(rows, n_q_heads, head_dim, S) + part_lse_bytes(rows, n_q_heads, S) + kSchedBytes;
 }
 
 size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
@@ -266,6 +285,9 @@ attn_status_t decode_common(const void *q, const void *k_cache, const void *v_ca
     a.part_o = static_cast<float *>(workspace);
     a.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
                                            part_o_bytes(batch * seqlen_q, n_q_heads, head_dim, S));
+    a.work_ctr = reinterpret_cast<unsigned *>(static_cast<char *>(workspace) +
+                                              part_o_bytes(batch * seqlen_q, n_q_heads, head_dim, S) +
+                                              part_lse_bytes(batch * seqlen_q, n_q_heads, S));
     a.o = static_cast<uint16_t *>(o);
     a.lse = lse;
     a.B = batch;

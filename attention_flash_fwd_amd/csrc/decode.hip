@@ -34,6 +34,8 @@
 // Kernel 2, decode_combine: one workgroup per (sequence, token, query head) merges
 //   the chunk partials: M = max lse_s, w_s = e^(lse_s - M),
 //   O = sum w_s O_s / sum w_s, lse = M + ln sum w_s; O rounded to bf16.
+#include <algorithm>
+
 #include "gfx950.hpp"
 #include "kernels.hpp"
 #include "../../include/attn.h"
@@ -49,6 +51,14 @@ constexpr int kWaves = 4;
 // their Q operands move to LDS (16 KiB, which with the 64 KiB ring still
 // lets two workgroups share a CU).
 constexpr int kMaxTiles = 4;
+// Split workgroups take their items from a work counter (staying resident)
+// for one or two column tiles; with more, each runs one item of a grid laid
+// out over the XCDs.  Measured on MI355X: the counter gains 1-4% where a
+// chunk is read in one pass, and loses up to 7% where several workgroups
+// share a chunk's reads through L2.
+template <int NCT>
+constexpr bool dynamic_items() { return NCT <= 2; }
+
 template <int D, int NCT>
 constexpr bool qs_in_lds() { return D == 128 && NCT == 4; }
 constexpr int kThreads = 64 * kWaves;
@@ -265,24 +275,54 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     uint8_t *const v_cv = aux;                          // [kWaves][block]
     uint8_t *const q_s = aux + kCv;
 
-    const int lane = threadIdx.x & 63;
     const int wave = (int)uniform_u32(threadIdx.x >> 6);
-    const int l16 = lane & 15, g = lane >> 4;
 
     const int G = a.Hq / a.Hkv;
     const int T = a.T;                  // new tokens per sequence
     const int GT = G * T;               // matrix-core columns in use: (token, head) pairs
-    // Workgroup -> (tile group, chunk, KV head, sequence).  Columns come in
-    // tiles of 16; a workgroup computes NCT consecutive tiles from one pass
-    // over its chunk.  Past NCT tiles, the groups of one (chunk, KV head,
-    // sequence) get ids 8 apart, so they run on the same XCD (ids go
-    // round-robin over the 8 XCDs) and share its L2 copy of the K/V blocks.
+    // Work item -> (tile group, chunk, KV head, sequence).  Columns come in
+    // tiles of 16; an item is NCT consecutive tiles computed from one pass
+    // over its chunk.
+    //  - One or two tiles (DYN): the workgroups stay resident and take items
+    //    from a counter in the workspace, so that workgroups on a faster XCD
+    //    take more of them.
+    //  - More tiles: one item per workgroup.  Past NCT tiles, the groups of
+    //    one (chunk, KV head, sequence) get ids 8 apart, so they run at the
+    //    same time on the same XCD (ids go round-robin over the 8 XCDs) and
+    //    share its L2 copy of the K/V blocks; a chunk is far larger than the
+    //    L2 share of one workgroup, so groups run one after another would
+    //    each read it from HBM.
+    constexpr bool DYN = dynamic_items<NCT>();
     const int n_ct = (GT + 15) / 16;
     const int n_grp = (n_ct + NCT - 1) / NCT;
-    const int L = blockIdx.x, r8 = L >> 3;
-    const int grp = r8 % n_grp;
-    const int unit = (r8 / n_grp) * 8 + (L & 7);
-    if (unit >= a.B * a.Hkv * a.splits) return;     // padding of the id space (uniform)
+    const unsigned n_units = (unsigned)(a.B * a.Hkv * a.splits);
+    // DYN: the item id is passed to the four waves through the first word of
+    // the ring, which is free between items; a third barrier keeps any wave
+    // from loading into the ring before all have read it.
+    unsigned *const item_slot = reinterpret_cast<unsigned *>(&k_s1[0][0]);
+    for (int round = 0;; ++round) {
+    int grp, unit;
+    if constexpr (DYN) {
+        __syncthreads();                // the previous item's LDS (ring, merge area) is free
+        if (threadIdx.x == 0) *item_slot = atomicAdd(a.work_ctr, 1u);
+        __syncthreads();
+        const unsigned item = uniform_u32(*item_slot);
+        __syncthreads();
+        if (item >= n_units * (unsigned)n_grp) break;
+        grp = (int)(item % (unsigned)n_grp);
+        unit = (int)(item / (unsigned)n_grp);
+    } else {
+        if (round > 0) break;
+        const int L = blockIdx.x, r8 = L >> 3;
+        grp = r8 % n_grp;
+        unit = (r8 / n_grp) * 8 + (L & 7);
+        if (unit >= (int)n_units) break;            // padding of the id space (uniform)
+    }
+    // DYN: lane index through opaque(), so that the per-lane addresses below
+    // are formed for each item, not hoisted out of the item loop into
+    // registers held across it.
+    const int lane = DYN ? opaque((int)(threadIdx.x & 63)) : (int)(threadIdx.x & 63);
+    const int l16 = lane & 15, g = lane >> 4;
     const int split = unit % a.splits;
     const int hk = (unit / a.splits) % a.Hkv;
     const int b = unit / (a.splits * a.Hkv);
@@ -499,6 +539,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
                 a.part_lse[row] = any_bad ? __builtin_nanf("") : (Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : kNegInf);
         }
     }
+    }   // items
+}
+
+// Zeroes the split kernel's work counter before each launch (a kernel, not a
+// memset, so that the sequence can be captured into a graph).
+__global__ void __launch_bounds__(64) decode_reset_kernel(unsigned *ctr)
+{
+    if (threadIdx.x == 0) ctr[0] = 0u;
 }
 
 // One workgroup per (sequence, query head).  Threads own 4 consecutive d of
@@ -592,14 +640,39 @@ __global__ void __launch_bounds__(kThreads) decode_combine_kernel(DecodeArgs a)
 template <int D, int EB, int NCT>
 constexpr unsigned occupancy_pad() { return (D == 128 && EB == 2 && NCT == 1) ? 32768u : 0u; }
 
+// Split workgroups resident on one CU at once (queried once per kernel).
+template <int D, int EB, int NCT>
+int resident_per_cu()
+{
+    static const int n = [] {
+        int v = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void *>(&decode_split_kernel<D, EB, NCT>),
+                                                         kThreads, occupancy_pad<D, EB, NCT>()) != hipSuccess || v <= 0)
+            v = 1;
+        return v;
+    }();
+    return n;
+}
+
 template <int D, int EB, int NCT>
 hipError_t launch_split(const DecodeArgs &a, long long n_ct, hipStream_t s)
 {
     const long long units = (long long)a.B * a.Hkv * a.splits;
-    const long long g1 = (units + 7) / 8 * 8 * ((n_ct + NCT - 1) / NCT);
-    if (g1 <= 0) return hipSuccess;
+    const long long n_grp = (n_ct + NCT - 1) / NCT;
+    if (units <= 0 || n_ct <= 0) return hipSuccess;
+    long long grid;
+    if constexpr (dynamic_items<NCT>()) {
+        // As many workgroups as the GPU holds at once, each taking items
+        // until the counter passes the last one.
+        grid = std::min<long long>(units * n_grp, (long long)resident_per_cu<D, EB, NCT>() * compute_units());
+        hipLaunchKernelGGL(decode_reset_kernel, dim3(1), dim3(64), 0, s, a.work_ctr);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else {
+        grid = (units + 7) / 8 * 8 * n_grp;         // ids padded to whole rounds over the XCDs
+    }
     constexpr unsigned pad = occupancy_pad<D, EB, NCT>();
-    hipLaunchKernelGGL((decode_split_kernel<D, EB, NCT>), dim3((unsigned)g1), dim3(kThreads), pad, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, EB, NCT>), dim3((unsigned)grid), dim3(kThreads), pad, s, a);
     return hipGetLastError();
 }
 

@@ -33,7 +33,11 @@ struct DecodeArgs {
     int B, T, Hq, Hkv, num_blocks, max_blocks, splits;
     float scale_log2;             // softmax scale (times the K dequantisation scale) times log2(e)
     float v_scale;                // V dequantisation scale (1 for bf16 caches)
+    unsigned *work_ctr;           // split-kernel work counter in the workspace (zeroed by the launch)
 };
+
+// Compute units of the current device (cached per device).
+int compute_units();
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, int head_dim, bool causal, hipStream_t s);

@@ -61,7 +61,6 @@
 // that a CU goes from one item to the next without waiting for a workgroup
 // to retire and another to be dispatched.
 #include <algorithm>
-#include <atomic>
 #include <type_traits>
 
 #include "gfx950.hpp"
@@ -614,20 +613,6 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int n_items)
     // K tile 0 lands there (the output stores may still be in flight).
     lds_barrier();
     }   // items
-}
-
-// Compute units of the current device (cached per device).
-int compute_units()
-{
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int v = cache[dev].load(std::memory_order_relaxed);
-    if (v <= 0) {
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-        cache[dev].store(v, std::memory_order_relaxed);
-    }
-    return v;
 }
 
 template <int D, bool CAUSAL, bool PAGED, int HPI>

@@ -169,8 +169,9 @@ int attn_decode_num_splits(int batch, int n_kv_heads, int max_blocks_per_seq,
  * attn_decode_workspace_bytes -- size of the scratch buffer attn_decode_paged
  * needs for these arguments: the per-chunk partial outputs
  * [batch, n_q_heads, splits, head_dim] fp32 followed by their log-sum-exps
- * [batch, n_q_heads, splits] fp32 (splits = attn_decode_num_splits(...)).
- * Returns 0 for invalid arguments.
+ * [batch, n_q_heads, splits] fp32 (splits = attn_decode_num_splits(...)),
+ * then 256 bytes of scheduling state (a work counter that every call resets
+ * on its stream before use).  Returns 0 for invalid arguments.
  */
 size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
                                    int max_blocks_per_seq, int block_size, int num_splits);
@@ -190,7 +191,9 @@ size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
  *   o            [batch, n_q_heads, head_dim] bf16, written
  *   lse          [batch, n_q_heads] fp32, written; may be NULL
  *   workspace    device scratch of at least attn_decode_workspace_bytes(...)
- *                bytes, 256-byte aligned; its contents on entry do not matter
+ *                bytes, 256-byte aligned; its contents on entry do not
+ *                matter.  Calls that overlap in time (on different streams)
+ *                need workspaces of their own.
  *
  * Every cached key of a sequence is visible to its query.  Sequence b's keys
  * are cut into `splits` chunks of equal length (a multiple of block_size,
@@ -293,7 +296,8 @@ attn_status_t attn_decode_paged_fp8(const void *q, const void *k_cache, const vo
  * partial outputs [batch, seqlen_q, n_q_heads, splits, head_dim] fp32, then
  * their log-sum-exps [batch, seqlen_q, n_q_heads, splits] fp32, with splits
  * the count attn_decode_paged_multi uses for these arguments
- * (attn_decode_num_splits when seqlen_q == 1).  Returns 0 for invalid
+ * (attn_decode_num_splits when seqlen_q == 1), then 256 bytes of scheduling
+ * state as for attn_decode_workspace_bytes.  Returns 0 for invalid
  * arguments.
  */
 size_t attn_decode_multi_workspace_bytes(int batch, int seqlen_q, int n_q_heads, int n_kv_heads,
