@@ -283,9 +283,15 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     // Work item -> (tile group, chunk, KV head, sequence).  Columns come in
     // tiles of 16; an item is NCT consecutive tiles computed from one pass
     // over its chunk.
-    //  - One or two tiles (DYN): the workgroups stay resident and take items
-    //    from a counter in the workspace, so that workgroups on a faster XCD
-    //    take more of them.
+    //  - One or two tiles (DYN): the workgroups stay resident.  Workgroup w
+    //    runs item w first; the items past the grid come from a counter in
+    //    the workspace, so that workgroups on a faster XCD take more of them.
+    //    Workgroup 0 zeroes the counter as it starts.  Whatever the counter
+    //    held before, no item is lost: a ticket taken before the reset
+    //    either lies past the end (that workgroup stops early) or is issued
+    //    again after it (the item is computed twice, with identical
+    //    results), and workgroup 0 keeps taking tickets until the counter
+    //    passes the last item.
     //  - More tiles: one item per workgroup.  Past NCT tiles, the groups of
     //    one (chunk, KV head, sequence) get ids 8 apart, so they run at the
     //    same time on the same XCD (ids go round-robin over the 8 XCDs) and
@@ -300,15 +306,24 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     // the ring, which is free between items; a third barrier keeps any wave
     // from loading into the ring before all have read it.
     unsigned *const item_slot = reinterpret_cast<unsigned *>(&k_s1[0][0]);
+    if (DYN && blockIdx.x == 0 && threadIdx.x == 0) atomicExch(a.work_ctr, 0u);
     for (int round = 0;; ++round) {
     int grp, unit;
     if constexpr (DYN) {
-        __syncthreads();                // the previous item's LDS (ring, merge area) is free
-        if (threadIdx.x == 0) *item_slot = atomicAdd(a.work_ctr, 1u);
-        __syncthreads();
-        const unsigned item = uniform_u32(*item_slot);
-        __syncthreads();
-        if (item >= n_units * (unsigned)n_grp) break;
+        const unsigned n_items = n_units * (unsigned)n_grp;
+        unsigned item = blockIdx.x;
+        if (round > 0) {
+            __syncthreads();            // the previous item's LDS (ring, merge area) is free
+            if (threadIdx.x == 0) {
+                // tickets 0, 1, ... stand for items gridDim.x, gridDim.x + 1, ...
+                const unsigned t = atomicAdd(a.work_ctr, 1u);
+                *item_slot = t < n_items - gridDim.x ? gridDim.x + t : n_items;
+            }
+            __syncthreads();
+            item = uniform_u32(*item_slot);
+            __syncthreads();
+        }
+        if (item >= n_items) break;
         grp = (int)(item % (unsigned)n_grp);
         unit = (int)(item / (unsigned)n_grp);
     } else {
@@ -542,12 +557,6 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     }   // items
 }
 
-// Zeroes the split kernel's work counter before each launch (a kernel, not a
-// memset, so that the sequence can be captured into a graph).
-__global__ void __launch_bounds__(64) decode_reset_kernel(unsigned *ctr)
-{
-    if (threadIdx.x == 0) ctr[0] = 0u;
-}
 
 // One workgroup per (sequence, query head).  Threads own 4 consecutive d of
 // one split row; the workgroup covers kThreads / (D / 4) splits at a time.
@@ -662,12 +671,9 @@ hipError_t launch_split(const DecodeArgs &a, long long n_ct, hipStream_t s)
     if (units <= 0 || n_ct <= 0) return hipSuccess;
     long long grid;
     if constexpr (dynamic_items<NCT>()) {
-        // As many workgroups as the GPU holds at once, each taking items
-        // until the counter passes the last one.
+        // As many workgroups as the GPU holds at once (never more than the
+        // items), each taking items until the counter passes the last one.
         grid = std::min<long long>(units * n_grp, (long long)resident_per_cu<D, EB, NCT>() * compute_units());
-        hipLaunchKernelGGL(decode_reset_kernel, dim3(1), dim3(64), 0, s, a.work_ctr);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
     } else {
         grid = (units + 7) / 8 * 8 * n_grp;         // ids padded to whole rounds over the XCDs
     }

@@ -170,8 +170,9 @@ int attn_decode_num_splits(int batch, int n_kv_heads, int max_blocks_per_seq,
  * needs for these arguments: the per-chunk partial outputs
  * [batch, n_q_heads, splits, head_dim] fp32 followed by their log-sum-exps
  * [batch, n_q_heads, splits] fp32 (splits = attn_decode_num_splits(...)),
- * then 256 bytes of scheduling state (a work counter that every call resets
- * on its stream before use).  Returns 0 for invalid arguments.
+ * then 256 bytes of scheduling state (a work counter, set by each call
+ * itself, so its contents on entry do not matter either).  Returns 0 for
+ * invalid arguments.
  */
 size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
                                    int max_blocks_per_seq, int block_size, int num_splits);

@@ -315,6 +315,38 @@ def test_decode_split_invariance_and_permutation(afa):
     assert torch.equal(o_a, o_c) and torch.equal(l_a, l_c), "repeat run differs"
 
 
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_workspace_contents_do_not_matter(afa, T):
+    # The workspace ends with the split kernel's work counter; whatever it
+    # holds on entry (huge, small or zero), every item is computed and the
+    # result is bit-identical to a call on a zeroed workspace.  T = 4 with
+    # G = 8 gives two column tiles, the other case scheduled by the counter.
+    from attention_flash_fwd_amd import inputs
+    say(f"case decode workspace garbage T{T}")
+    # 5 sequences x 8 KV heads x 16 chunks = 640 items, more than the GPU
+    # holds at once, so that some items come from the counter.
+    inp = gen_decode([3000, 17, 900, 4096, 1], 64, 8, 128, seed=12)
+    q = inputs.chunk_queries(inp.batch, T, 64, 128, seed=13, device="cuda")
+    ws = afa.decode_workspace(q, inp.k_cache, inp.block_table, 16)
+    ws.zero_()
+    ref = afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                 num_splits=16, workspace=ws)
+    torch.cuda.synchronize()
+    tail = ws[-256:].view(torch.int32)
+    for fill in (-1, 1, 0x7fffffff, 5):
+        tail.fill_(fill)
+        o, l = afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                      num_splits=16, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[0]) and torch.equal(l, ref[1]), f"counter fill {fill}"
+    # Calls in a row reuse the counter as the previous call left it.
+    for _ in range(3):
+        o, l = afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                      num_splits=16, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref[0]) and torch.equal(l, ref[1])
+
+
 def test_decode_contract_violations_give_nan(afa):
     say("case decode bad block ids / oversize ctx")
     inp = gen_decode([40, 40, 40], 8, 2, 128, seed=8, table_pad=0)
