@@ -126,3 +126,52 @@ def test_decode_random(afa, seed):
     o_ref, l_ref = oracle_paged(inp, q, True, scale)
     check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
     check_lse(to_np(lse), l_ref, BF16_LSE_ABS)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_random_many_items(afa, seed):
+    # More (chunk, KV head, sequence) items than the GPU holds split
+    # workgroups at once, with one or two column tiles (G T <= 32), so that
+    # most items are handed out by the split kernel's work counter; the
+    # ragged lengths (some empty) make items of very different cost.  Odd
+    # seeds read an fp8 cache.
+    from attention_flash_fwd_amd import inputs
+    rng = np.random.default_rng(9500 + seed)
+    fp8 = seed % 2 == 1
+    nseq = int(rng.integers(32, 49))
+    Hkv = int(rng.choice([4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hq = Hkv * G
+    T = 1 if seed < 2 else int(rng.integers(1, 32 // G + 1))
+    D = int(rng.choice([64, 128]))
+    ctx = [0 if rng.random() < 0.1 else int(rng.integers(1, 2500)) for _ in range(nseq)]
+    splits = int(rng.choice([24, 32]))
+    ks, vs = (0.03, 0.05) if fp8 else (1.0, 1.0)
+    say(f"case random decode, many items, seed{seed}: nseq{nseq} T{T} Hq{Hq} Hkv{Hkv} D{D} "
+        f"splits{splits} {'fp8' if fp8 else 'bf16'} ctx[:6]{ctx[:6]}")
+    inp = inputs.decode_inputs(ctx, Hq, Hkv, D, seed=800 + seed, device="cuda", spare_blocks=2,
+                               kv_format="fp8" if fp8 else "bf16", k_scale=ks, v_scale=vs)
+    q = inputs.chunk_queries(nseq, T, Hq, D, seed=800 + seed, device="cuda")
+    scale = 1 / math.sqrt(D)
+    if fp8:
+        o, lse = afa.decode_paged_fp8(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens, ks, vs,
+                                      num_splits=splits, scale=scale)
+    else:
+        o, lse = afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                        num_splits=splits, scale=scale)
+    torch.cuda.synchronize()
+    if fp8:
+        qn = to_np(q)
+        os_, ls_ = [], []
+        for b in range(nseq):
+            kb, vb = inp.logical_kv(b, device="cpu")
+            k = oracle.e4m3_decode(kb.numpy()).astype(np.float32)[None]
+            v = oracle.e4m3_decode(vb.numpy()).astype(np.float32)[None]
+            ob, lb = oracle.attention(qn[b:b + 1], k, v, True, scale * ks)
+            os_.append(ob[0] * vs)
+            ls_.append(lb[0])
+        o_ref, l_ref = np.stack(os_), np.stack(ls_)
+    else:
+        o_ref, l_ref = oracle_paged(inp, q, True, scale)
+    check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse), l_ref, BF16_LSE_ABS)
