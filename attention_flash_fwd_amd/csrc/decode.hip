@@ -7,8 +7,11 @@
 // "抱infra脚", section Paged Attention: fixed-size blocks reached through a
 // block table).
 //
-// Kernel 1, decode_split: one workgroup of four waves per (chunk, KV head,
-//   sequence).  The G = Hq / Hkv query heads that share the KV head, times
+// Kernel 1, decode_split: a workgroup of four waves computes one (chunk, KV
+//   head, sequence) item at a time.  With one or two column tiles (below),
+//   as many workgroups as the GPU holds stay resident and take items from a
+//   work counter in the workspace; with more, each workgroup computes one
+//   item.  The G = Hq / Hkv query heads that share the KV head, times
 //   the T new tokens of the sequence (T = 1 for plain decode, several for
 //   speculative verification), are the columns of the matrix-core products,
 //   so each K/V byte is read from HBM once for all of them.  The chunk's
@@ -302,10 +305,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     const int n_ct = (GT + 15) / 16;
     const int n_grp = (n_ct + NCT - 1) / NCT;
     const unsigned n_units = (unsigned)(a.B * a.Hkv * a.splits);
-    // DYN: the item id is passed to the four waves through the first word of
-    // the ring, which is free between items; a third barrier keeps any wave
-    // from loading into the ring before all have read it.
-    unsigned *const item_slot = reinterpret_cast<unsigned *>(&k_s1[0][0]);
+    // DYN: thread 0 takes the next item's ticket while the current item's
+    // partials merge (hiding the atomic's latency) and passes the item id to
+    // the four waves through an LDS word of its own.  One barrier per item
+    // suffices: a wave reaches it only once done with the previous item, and
+    // thread 0 writes the word again only after the item's own barriers,
+    // which every wave passes after reading it.
+    __shared__ unsigned item_slot[1];
+    unsigned ticket = 0;                // thread 0: the ticket for the next item
     if (DYN && blockIdx.x == 0 && threadIdx.x == 0) atomicExch(a.work_ctr, 0u);
     for (int round = 0;; ++round) {
     int grp, unit;
@@ -313,15 +320,11 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
         const unsigned n_items = n_units * (unsigned)n_grp;
         unsigned item = blockIdx.x;
         if (round > 0) {
-            __syncthreads();            // the previous item's LDS (ring, merge area) is free
-            if (threadIdx.x == 0) {
-                // tickets 0, 1, ... stand for items gridDim.x, gridDim.x + 1, ...
-                const unsigned t = atomicAdd(a.work_ctr, 1u);
-                *item_slot = t < n_items - gridDim.x ? gridDim.x + t : n_items;
-            }
+            // tickets 0, 1, ... stand for items gridDim.x, gridDim.x + 1, ...
+            if (threadIdx.x == 0)
+                item_slot[0] = ticket < n_items - gridDim.x ? gridDim.x + ticket : n_items;
             __syncthreads();
-            item = uniform_u32(*item_slot);
-            __syncthreads();
+            item = uniform_u32(item_slot[0]);
         }
         if (item >= n_items) break;
         grp = (int)(item % (unsigned)n_grp);
@@ -474,6 +477,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     // barrier.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (DYN && threadIdx.x == 0) ticket = atomicAdd(a.work_ctr, 1u);
     // Wave w's partial O (16 columns x D fp32): bf16 caches put two waves in
     // each of k_s0 / v_s0, fp8 caches one wave in each of the four slots.
     auto merge_area = [&](int v) __attribute__((always_inline)) -> float * {
