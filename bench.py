@@ -48,7 +48,65 @@ def parse():
     p.add_argument("--parts", default="prefill,decode_b64,decode_128k," + ",".join(EXTRAS),
                    help="comma-separated subset (for profiling runs); 'copy' adds a plain "
                         "1 GiB device-to-device copy that calibrates the HBM byte counters")
+    p.add_argument("--compare-sdpa", action="store_true",
+                   help="instead of the benchmark, time PyTorch's fused attention (SDPA, flash "
+                        "backend) beside attn_prefill on the prefill workload; one JSON line")
     return p.parse_args()
+
+
+def compare_sdpa(steps, warmup):
+    """Context, not the benchmark: PyTorch's fused attention on the same
+    causal GQA prefill input as attn_prefill.  Only the flash backend is
+    allowed, so an unsupported case raises instead of falling back to the
+    bf16 math path.  K and V are expanded to the query heads beforehand
+    (untimed), since the call is made without a GQA layout."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    import attention_flash_fwd_amd as afa
+    from attention_flash_fwd_amd import _lib, inputs
+
+    _lib.load()
+    cfg = inputs.PREFILL_8K
+    q, k, v = inputs.prefill_config_inputs(cfg, device=torch.device("cuda:0"))     # [B, S, H, D]
+    rep_ = q.shape[2] // k.shape[2]
+    qt = q.transpose(1, 2).contiguous()
+    kt = k.repeat_interleave(rep_, dim=2).transpose(1, 2).contiguous()
+    vt = v.repeat_interleave(rep_, dim=2).transpose(1, 2).contiguous()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    def sdpa():
+        return F.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+
+    # Three interleaved rounds, the best of each, so that neither side is
+    # timed alone on a cold or a hot chip.
+    ours_ms = sdpa_ms = float("inf")
+    with sdpa_kernel(SDPBackend.FLASH_ATTENTION):
+        for _ in range(3):
+            ours_ms = min(ours_ms, timed(lambda: afa.prefill(q, k, v, causal=True, return_lse=False)))
+            sdpa_ms = min(sdpa_ms, timed(sdpa))
+        o_sdpa = sdpa().transpose(1, 2)
+    o_ours, _ = afa.prefill(q, k, v, causal=True, return_lse=False)
+    torch.cuda.synchronize()
+    flops = cfg.flops()
+    print(json.dumps({"compare": "torch_sdpa_flash", "workload": cfg.name, "torch": torch.__version__,
+                      "attn_prefill_ms": ours_ms, "attn_prefill_tflops": flops / ours_ms / 1e9,
+                      "sdpa_ms": sdpa_ms, "sdpa_tflops": flops / sdpa_ms / 1e9,
+                      "speedup": sdpa_ms / ours_ms,
+                      "max_abs_diff": (o_sdpa.float() - o_ours.float()).abs().max().item()}))
 
 
 def decode_bytes(inp, n_q_heads):
@@ -157,6 +215,9 @@ def cpu_baseline(parts, pf_cfg, pf_in, dec_parts):
 
 def main():
     args = parse()
+    if args.compare_sdpa:
+        compare_sdpa(args.steps, args.warmup)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path).", file=sys.stderr)
