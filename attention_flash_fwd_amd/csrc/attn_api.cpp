@@ -271,6 +271,10 @@ attn_status_t decode_common(const void *q, const void *k_cache, const void *v_ca
 
     const int S = resolve_splits_multi(batch, seqlen_q, n_q_heads, n_kv_heads, max_blocks_per_seq, block_size,
                                        num_splits);
+    // Split-kernel work items (chunk, KV head, sequence, group of up to 4
+    // column tiles of 16) are numbered in 32 bits.
+    const long long col_tiles = ((long long)(n_q_heads / n_kv_heads) * seqlen_q + 15) / 16;
+    if ((long long)batch * n_kv_heads * S * ((col_tiles + 3) / 4) >= (1LL << 31)) return ATTN_ERR_SHAPE;
     const size_t need = attn_decode_multi_workspace_bytes(batch, seqlen_q, n_q_heads, n_kv_heads, head_dim,
                                                           max_blocks_per_seq, block_size, num_splits);
     if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;

@@ -204,7 +204,9 @@ size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
  * they may hold anything, NaN included.
  *
  * Supported: head_dim 64 or 128; block_size 16; n_q_heads / n_kv_heads <= 256;
- * num_splits in [1, ATTN_MAX_SPLITS] or <= 0 for the library's choice.
+ * num_splits in [1, ATTN_MAX_SPLITS] or <= 0 for the library's choice;
+ * batch * n_kv_heads * splits < 2^31 (ATTN_ERR_SHAPE otherwise; with several
+ * new tokens, times the groups of up to 64 (head, token) columns).
  * ctx_lens[b] == 0 gives O = 0, lse = -inf.
  * Device-side contract violations do not fault: a sequence whose ctx_lens
  * entry is negative or exceeds max_blocks_per_seq * block_size, or whose

@@ -196,6 +196,14 @@ def test_decode_fp8_validation(lib):
     assert decode_fp8(lib, B=0, q=0) == OK
 
 
+def test_decode_item_count_limit(lib):
+    # 2^20 sequences x 8 KV heads x 256 chunks = 2^31 split-kernel items:
+    # rejected before any launch (the element counts alone are in range).
+    assert decode_multi(lib, T=1, B=1 << 20, Hq=8, Hkv=8, D=64, max_blocks=1, splits=256) == SHAPE
+    assert decode_multi(lib, T=1, B=(1 << 20) - 1, Hq=8, Hkv=8, D=64, max_blocks=1, splits=256,
+                        ws=0) == WORKSPACE
+
+
 def test_workspace_and_split_rules(lib):
     # Explicit split counts pass through; the workspace holds fp32 partial
     # outputs and log-sum-exps for every (sequence, query head, split), then
