@@ -175,3 +175,90 @@ def test_decode_random_many_items(afa, seed):
         o_ref, l_ref = oracle_paged(inp, q, True, scale)
     check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
     check_lse(to_np(lse), l_ref, BF16_LSE_ABS)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_decode_random_sweep(afa, seed):
+    # Wider draws than test_decode_random: up to 48 sequences (some empty),
+    # every column-tile count up to 16 (G T <= 256 with T <= 32), explicit
+    # or automatic split counts, bf16 or fp8 caches with random scales.
+    from attention_flash_fwd_amd import inputs
+    rng = np.random.default_rng(12000 + seed)
+    fp8 = bool(rng.random() < 0.4)
+    nseq = int(rng.integers(1, 49))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
+    Hq = Hkv * G
+    T = int(rng.integers(1, 256 // G + 1)) if rng.random() < 0.3 else int(rng.integers(1, 5))
+    T = min(T, 32)
+    D = int(rng.choice([64, 128]))
+    ctx = [0 if rng.random() < 0.08 else int(rng.integers(1, 2000)) for _ in range(nseq)]
+    splits = int(rng.choice([0, 1, 7, 16, 32, 64]))
+    ks, vs = (float(rng.uniform(0.02, 0.06)), float(rng.uniform(0.02, 0.06))) if fp8 else (1.0, 1.0)
+    say(f"case random decode sweep seed{seed}: nseq{nseq} T{T} Hq{Hq} Hkv{Hkv} D{D} splits{splits} "
+        f"{'fp8' if fp8 else 'bf16'}")
+    inp = inputs.decode_inputs(ctx, Hq, Hkv, D, seed=900 + seed, device="cuda", spare_blocks=2,
+                               kv_format="fp8" if fp8 else "bf16", k_scale=ks, v_scale=vs)
+    q = inputs.chunk_queries(nseq, T, Hq, D, seed=900 + seed, device="cuda")
+    scale = 1 / math.sqrt(D)
+    if fp8:
+        o, lse = afa.decode_paged_fp8(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens, ks, vs,
+                                      num_splits=splits, scale=scale)
+    else:
+        o, lse = afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                        num_splits=splits, scale=scale)
+    torch.cuda.synchronize()
+    qn = to_np(q)
+    os_, ls_ = [], []
+    for b in range(nseq):
+        kb, vb = inp.logical_kv(b, device="cpu")
+        if fp8:
+            k = oracle.e4m3_decode(kb.numpy()).astype(np.float32)[None]
+            v = oracle.e4m3_decode(vb.numpy()).astype(np.float32)[None]
+            ob, lb = oracle.attention(qn[b:b + 1], k, v, True, scale * ks)
+            ob = ob * vs
+        else:
+            ob, lb = oracle.attention(qn[b:b + 1], kb.float().numpy()[None], vb.float().numpy()[None], True, scale)
+        os_.append(ob[0])
+        ls_.append(lb[0])
+    check_o(to_np(o), np.stack(os_), BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse), np.stack(ls_), BF16_LSE_ABS)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_prefill_random_sweep(afa, seed):
+    # Wider draws than test_prefill_random / test_prefill_paged_random:
+    # lengths up to about 1100, contiguous or paged keys.
+    from attention_flash_fwd_amd import inputs
+    rng = np.random.default_rng(15000 + seed)
+    Hq, Hkv = heads(rng)
+    D = int(rng.choice([64, 128]))
+    causal = bool(rng.random() < 0.7)
+    scale = 1 / math.sqrt(D)
+    if rng.random() >= 0.4:
+        B = int(rng.integers(1, 4))
+        Sq = int(rng.integers(1, 1100))
+        Sk = Sq if rng.random() < 0.5 else int(rng.integers(1, 1100))
+        while B * Hq * Sq * Sk > MAX_PAIRS:
+            Sq, Sk = max(1, Sq * 3 // 4), max(1, Sk * 3 // 4)
+        say(f"case random prefill sweep seed{seed}: B{B} Sq{Sq} Sk{Sk} Hq{Hq} Hkv{Hkv} D{D} causal{causal}")
+        q, k, v = inputs.prefill_inputs(B, Sq, Sk, Hq, Hkv, D, torch.bfloat16, 3000 + seed, device="cpu")
+        o, lse = afa.prefill(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention(to_np(q), to_np(k), to_np(v), causal, scale)
+    else:
+        nseq = int(rng.integers(1, 6))
+        ctx = [int(rng.integers(0, 1200)) for _ in range(nseq)]
+        Sq = int(rng.integers(1, 600))
+        while nseq * Hq * Sq * max(max(ctx), 1) > MAX_PAIRS:
+            Sq = max(1, Sq * 3 // 4)
+            ctx = [c * 3 // 4 for c in ctx]
+        say(f"case random prefill_paged sweep seed{seed}: ctx{ctx} Sq{Sq} Hq{Hq} Hkv{Hkv} D{D} causal{causal}")
+        inp = inputs.decode_inputs(ctx, Hq, Hkv, D, seed=4000 + seed, device="cuda", spare_blocks=2)
+        q = inputs.chunk_queries(nseq, Sq, Hq, D, seed=4000 + seed, device="cuda")
+        o, lse = afa.prefill_paged(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                   causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle_paged(inp, q, causal, scale)
+    check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse), l_ref, BF16_LSE_ABS)
