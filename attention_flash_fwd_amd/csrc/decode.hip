@@ -37,6 +37,8 @@
 // Kernel 2, decode_combine: one workgroup per (sequence, token, query head) merges
 //   the chunk partials: M = max lse_s, w_s = e^(lse_s - M),
 //   O = sum w_s O_s / sum w_s, lse = M + ln sum w_s; O rounded to bf16.
+//   With a single chunk the merge is the identity (w = 1), so the split
+//   kernel writes O and lse itself and this kernel is not launched.
 #include <algorithm>
 
 #include "gfx950.hpp"
@@ -544,18 +546,34 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
                 }
             }
             const int gcol = col0 + hh;
-            const size_t row = (((size_t)b * T + gcol / G) * a.Hq + hk * G + gcol % G) * a.splits + split;
-            float *dst = a.part_o + row * D + dq * DPT;
+            const int tq = gcol / G, hq = hk * G + gcol % G;        // new token, query head
+            const size_t orow = ((size_t)b * T + tq) * a.Hq + hq;
 #pragma unroll
-            for (int i = 0; i < DPT; i += 4) {
-                f32x4_t y;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] = Ls > 0.f ? o[i + e] / Ls * a.v_scale : 0.f;
-                if (any_bad) y = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-                *reinterpret_cast<f32x4_t *>(dst + i) = y;
+            for (int i = 0; i < DPT; ++i) {
+                o[i] = Ls > 0.f ? o[i] / Ls * a.v_scale : 0.f;
+                if (any_bad) o[i] = __builtin_nanf("");
             }
-            if (dq == 0)
-                a.part_lse[row] = any_bad ? __builtin_nanf("") : (Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : kNegInf);
+            const float lse = any_bad ? __builtin_nanf("") : (Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : kNegInf);
+            if (a.splits == 1) {
+                // A single chunk is the whole result (the merge would weigh it
+                // by e^0 = 1): bf16 output and lse straight from here.
+                uint32_t pk2[DPT / 2];
+#pragma unroll
+                for (int i = 0; i < DPT / 2; ++i) pk2[i] = pack_bf16x2(o[2 * i], o[2 * i + 1]);
+                uint16_t *dsto = a.o + orow * D + dq * DPT;
+                if constexpr (DPT == 8)
+                    *reinterpret_cast<u32x4_t *>(dsto) = u32x4_t{pk2[0], pk2[1], pk2[2], pk2[3]};
+                else
+                    *reinterpret_cast<u32x2_t *>(dsto) = u32x2_t{pk2[0], pk2[1]};
+                if (dq == 0 && a.lse != nullptr) a.lse[((size_t)b * a.Hq + hq) * T + tq] = lse;
+            } else {
+                const size_t row = orow * a.splits + split;
+                float *dst = a.part_o + row * D + dq * DPT;
+#pragma unroll
+                for (int i = 0; i < DPT; i += 4)
+                    *reinterpret_cast<f32x4_t *>(dst + i) = f32x4_t{o[i], o[i + 1], o[i + 2], o[i + 3]};
+                if (dq == 0) a.part_lse[row] = lse;
+            }
         }
     }
     }   // items
@@ -702,6 +720,7 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
     else e = launch_split<D, EB, kMaxTiles>(a, n_ct, s);
     if (n_ct <= 0 || (long long)a.B * a.Hkv * a.splits <= 0) return e;
     if (e != hipSuccess) return e;
+    if (a.splits == 1) return hipSuccess;          // the split kernel wrote the result itself
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.B * a.T * a.Hq)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }

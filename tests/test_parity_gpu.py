@@ -347,6 +347,36 @@ def test_decode_workspace_contents_do_not_matter(afa, T):
     assert torch.equal(o, ref[0]) and torch.equal(l, ref[1])
 
 
+@pytest.mark.parametrize("fp8,D,T", [(False, 128, 1), (False, 64, 3), (True, 128, 1), (True, 128, 3)])
+def test_decode_single_split_writes_result_directly(afa, fp8, D, T):
+    # With one chunk the split kernel writes bf16 O and lse itself (no merge
+    # kernel).  Contexts of at most 16 tokens make a second chunk empty, so
+    # two chunks go through the merge with weights exactly 1 and 0: the
+    # results must be bit-identical, empty sequences included.
+    from attention_flash_fwd_amd import inputs
+    say(f"case decode single split fp8={fp8} D{D} T{T}")
+    ctx = [16, 1, 0, 9, 16, 5, 12]
+    inp = inputs.decode_inputs(ctx, 32, 8, D, seed=21, device="cuda", spare_blocks=2,
+                               kv_format="fp8" if fp8 else "bf16", k_scale=0.03, v_scale=0.05)
+    q = inputs.chunk_queries(len(ctx), T, 32, D, seed=22, device="cuda")
+    if fp8:
+        run = lambda s, lse=True: afa.decode_paged_fp8(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                                       0.03, 0.05, num_splits=s, return_lse=lse)
+    else:
+        run = lambda s, lse=True: afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, inp.block_table,
+                                                         inp.ctx_lens, num_splits=s, return_lse=lse)
+    o1, l1 = run(1)
+    o2, l2 = run(2)
+    o3, l3 = run(1, lse=False)
+    torch.cuda.synchronize()
+    assert l3 is None
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+    assert torch.equal(torch.isneginf(l1), torch.isneginf(l2))
+    fin = torch.isfinite(l1)
+    assert torch.equal(l1[fin], l2[fin])
+    assert torch.all(o1[2] == 0) and torch.all(torch.isneginf(l1[2]))
+
+
 def test_decode_contract_violations_give_nan(afa):
     say("case decode bad block ids / oversize ctx")
     inp = gen_decode([40, 40, 40], 8, 2, 128, seed=8, table_pad=0)
