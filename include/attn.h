@@ -159,8 +159,9 @@ attn_status_t attn_prefill_paged(const void *q, const void *k_cache, const void 
  * num_splits <= 0 asks for the library's choice, which depends only on the
  * arguments given here (never on device data): chunks of about 2048 tokens
  * of the longest sequence the table can hold, or more chunks (none shorter
- * than 256 tokens) when that is needed for about 2048 workgroups to occupy
- * the GPU.  Returns 0 for invalid arguments.
+ * than 256 tokens) when that is needed for about 256 (chunk, sequence, KV
+ * head) items, one per compute unit, to occupy the GPU.  Returns 0 for
+ * invalid arguments.
  */
 int attn_decode_num_splits(int batch, int n_kv_heads, int max_blocks_per_seq,
                            int block_size, int num_splits);

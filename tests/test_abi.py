@@ -221,7 +221,12 @@ def test_workspace_and_split_rules(lib):
         assert 1 <= s <= 256
         assert s <= max(1, (mb * 16 + 255) // 256)
         if (mb * 16) // 256 >= 256:
-            assert B * Hkv * s >= 1024
+            assert B * Hkv * s >= 256
+    # The library's choice on the two decode workloads and on shapes where
+    # one chunk per sequence already gives one item per compute unit.
+    for (B, Hkv, mb), want in [((64, 8, 2048), 16), ((4, 8, 8192), 64), ((32, 8, 64), 1),
+                               ((128, 8, 32), 1), ((16, 8, 128), 2), ((8, 8, 256), 4), ((1, 8, 1024), 32)]:
+        assert lib.attn_decode_num_splits(B, Hkv, mb, 16, 0) == want, (B, Hkv, mb)
     assert lib.attn_decode_num_splits(-1, 8, 4, 16, 0) == 0
     assert lib.attn_decode_workspace_bytes(1, 0, 1, 128, 4, 16, 1) == 0
 
