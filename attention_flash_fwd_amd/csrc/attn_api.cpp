@@ -74,8 +74,11 @@ int resolve_splits(int batch, int n_kv_heads, int max_blocks, int block_size, in
 // query head), so with C = (n_q_heads / n_kv_heads) * seqlen_q columns the
 // partial traffic grows with C.  The chunks are then longer, about
 // 2048 * min(4, max(1, C / 4)) tokens of the longest sequence.  More chunks
-// (none shorter than 256 tokens) are used only until about 512 workgroups,
-// counted with the column-tile groups, occupy the GPU.  (Measured on
+// (none shorter than 256 tokens) are used only until about 256 items, one
+// per compute unit and counted with the column-tile groups, occupy the GPU
+// (as for one token; short contexts at 2-8 tokens measured best there, e.g.
+// 32 sequences of 1024 tokens at one chunk, 25 us against 35 us at the two
+// a 512 target gave).  (Measured on
 // MI355X against the single-token rule: batch 64 with contexts up to 32K,
 // 2-8 tokens: 3-5% faster; batch 4 at 128K, 8 tokens: 14% faster, 2-4
 // tokens within 1%.)
@@ -92,7 +95,7 @@ int resolve_splits_multi(int batch, int seqlen_q, int n_q_heads, int n_kv_heads,
     const long long groups = ((cols + 15) / 16 + 3) / 4;     // workgroups per (chunk, sequence, KV head)
     const long long by_length = (max_tokens + 2048 * f - 1) / (2048 * f);
     const long long wgs = units * groups;
-    const long long by_fill = std::min((512 + wgs - 1) / wgs, (max_tokens + 255) / 256);
+    const long long by_fill = std::min((kFillItems + wgs - 1) / wgs, (max_tokens + 255) / 256);
     long long s = std::max(by_length, by_fill);
     if (s > ATTN_MAX_SPLITS) s = ATTN_MAX_SPLITS;
     if (s < 1) s = 1;

@@ -252,7 +252,8 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
  * head), so with C = (n_q_heads / n_kv_heads) * seqlen_q the chunks are
  * about 2048 * min(4, max(1, C / 4)) tokens of the longest sequence the
  * table can hold.  More chunks (none shorter than 256 tokens) are used only
- * until about 512 workgroups occupy the GPU.  attn_decode_multi_workspace_bytes
+ * until about 256 items (chunk, sequence, KV head, group of up to 64
+ * columns) occupy the GPU.  attn_decode_multi_workspace_bytes
  * sizes the workspace for the same choice.
  */
 attn_status_t attn_decode_paged_multi(const void *q, const void *k_cache, const void *v_cache,

@@ -246,12 +246,15 @@ def test_multi_token_split_rule(lib):
         assert multi_splits(lib, B, 1, Hq, Hkv, 128, mb, 0) == lib.attn_decode_num_splits(B, Hkv, mb, 16, 0)
         assert multi_splits(lib, B, 4, Hq, Hkv, 128, mb, 7) == 7
     # Several tokens: chunks of 2048 * min(4, max(1, C / 4)) tokens of the
-    # longest sequence, C = G * T columns, or more chunks up to about 512
-    # workgroups (column-tile groups of 4 x 16 columns each count).
+    # longest sequence, C = G * T columns, or more chunks up to about 256
+    # items (column-tile groups of 4 x 16 columns each count).
     assert multi_splits(lib, 64, 2, 32, 8, 128, 2048, 0) == 8      # C = 8:  chunks of 4096 tokens
     assert multi_splits(lib, 64, 4, 32, 8, 128, 2048, 0) == 4      # C = 16: chunks of 8192 tokens
     assert multi_splits(lib, 64, 8, 32, 8, 128, 2048, 0) == 4      # C = 32: capped at 4 x 2048
-    assert multi_splits(lib, 4, 8, 64, 8, 128, 8192, 0) == 16      # 32 (seq, KV head) pairs: 512 / 32
+    assert multi_splits(lib, 4, 8, 64, 8, 128, 8192, 0) == 16      # C = 64: 131072 / 8192
+    assert multi_splits(lib, 32, 4, 32, 8, 128, 64, 0) == 1        # 256 (seq, KV head) pairs already
+    assert multi_splits(lib, 8, 4, 32, 8, 128, 256, 0) == 4        # 64 pairs: 256 / 64
+    assert multi_splits(lib, 1, 2, 32, 8, 128, 1024, 0) == 32      # 8 pairs: 256 / 8
     assert multi_splits(lib, 1, 2, 8, 8, 64, 4, 0) == 1            # 64 tokens: one chunk of at least 256
     for B, T, Hq, Hkv, mb in [(1, 3, 4, 1, 1), (2, 16, 16, 1, 300), (8, 5, 64, 8, 9000)]:
         s = multi_splits(lib, B, T, Hq, Hkv, 64, mb, 0)
