@@ -16,7 +16,8 @@ import math
 from . import _lib
 from ._lib import AttnError, MAX_SPLITS  # noqa: F401
 
-__all__ = ["prefill", "decode_paged", "decode_num_splits", "decode_workspace_bytes",
+__all__ = ["prefill", "prefill_paged", "decode_paged", "decode_paged_multi", "decode_paged_fp8",
+           "decode_num_splits", "decode_workspace_bytes",
            "decode_workspace", "AttnError", "library_path"]
 
 
@@ -46,6 +47,33 @@ def _need_gpu(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _same_device(ref, *ts):
+    for t in ts:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"all tensors must be on {ref.device}; got one on {t.device}")
+
+
+def _check_out(t, shape, dtype, name):
+    """A caller-supplied output must have exactly the shape and dtype the
+    kernels write: the C ABI takes raw pointers and cannot see a short or
+    mistyped buffer, so this is the last place that can refuse one."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}; expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}; expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(ws):
+    # The library checks the workspace's byte count itself; it must be one
+    # flat byte buffer so that numel() is that count.
+    if ws is not None and (ws.dim() != 1 or ws.element_size() != 1 or not ws.is_contiguous()):
+        raise ValueError("workspace must be a contiguous 1-D byte tensor (see decode_workspace)")
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else 0)
 
@@ -57,13 +85,16 @@ def prefill(q, k, v, causal: bool = True, scale: float | None = None, out=None, 
     Returns (o [B,Sq,Hq,D] in q's dtype, lse [B,Hq,Sq] fp32 or None)."""
     import torch
     lib = _lib.load()
-    _need_gpu(q, k, v, out, lse_out)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("expected q [B,Sq,Hq,D] and k, v [B,Sk,Hkv,D]")
     B, Sq, Hq, D = q.shape
     Sk, Hkv = k.shape[1], k.shape[2]
     if k.shape[0] != B or k.shape[3] != D or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v disagree in batch, head_dim or dtype")
+    _check_out(out, q.shape, q.dtype, "out")
+    _check_out(lse_out, (B, Hq, Sq), torch.float32, "lse_out")
+    _need_gpu(q, k, v, out, lse_out)
+    _same_device(q, k, v, out, lse_out)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = out if out is not None else torch.empty_like(q)
@@ -114,15 +145,20 @@ def prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, causal: bool = Tru
     included).  Returns (o [B,Sq,Hq,D] bf16, lse [B,Hq,Sq] fp32 or None)."""
     import torch
     lib = _lib.load()
-    _need_gpu(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out)
     if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
         raise TypeError("prefill_paged takes bf16 q and caches")
     if block_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
         raise TypeError("block_table and ctx_lens must be int32")
+    if q.dim() != 4 or k_cache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("expected q [B,Sq,Hq,D], caches [num_blocks,16,Hkv,D], block_table [B,max_blocks]")
     B, Sq, Hq, D = q.shape
     nblocks, bs, Hkv, Dk = k_cache.shape
     if Dk != D or v_cache.shape != k_cache.shape or block_table.shape[0] != B or ctx_lens.shape != (B,):
         raise ValueError("inconsistent prefill_paged shapes")
+    _check_out(out, q.shape, torch.bfloat16, "out")
+    _check_out(lse_out, (B, Hq, Sq), torch.float32, "lse_out")
+    _need_gpu(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out)
+    _same_device(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = out if out is not None else torch.empty_like(q)
@@ -147,15 +183,21 @@ def decode_paged_multi(q, k_cache, v_cache, block_table, ctx_lens, num_splits: i
     Returns (o [B,T,Hq,D] bf16, lse [B,Hq,T] fp32 or None)."""
     import torch
     lib = _lib.load()
-    _need_gpu(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out, workspace)
     if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
         raise TypeError("decode_paged_multi takes bf16 q and caches")
     if block_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
         raise TypeError("block_table and ctx_lens must be int32")
+    if q.dim() != 4 or k_cache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("expected q [B,T,Hq,D], caches [num_blocks,16,Hkv,D], block_table [B,max_blocks]")
     B, T, Hq, D = q.shape
     nblocks, bs, Hkv, Dk = k_cache.shape
     if Dk != D or v_cache.shape != k_cache.shape or block_table.shape[0] != B or ctx_lens.shape != (B,):
         raise ValueError("inconsistent decode shapes")
+    _check_out(out, q.shape, torch.bfloat16, "out")
+    _check_out(lse_out, (B, Hq, T), torch.float32, "lse_out")
+    _check_workspace(workspace)
+    _need_gpu(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out, workspace)
+    _same_device(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out, workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if workspace is None:
@@ -182,17 +224,24 @@ def decode_paged_fp8(q, k_cache, v_cache, block_table, ctx_lens, k_scale: float,
     codes.  Returns (o, lse) shaped like decode_paged / decode_paged_multi."""
     import torch
     lib = _lib.load()
-    _need_gpu(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out, workspace)
     if q.dtype != torch.bfloat16 or k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
         raise TypeError("decode_paged_fp8 takes bf16 q and uint8 (e4m3) caches")
     if block_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
         raise TypeError("block_table and ctx_lens must be int32")
+    if q.dim() not in (3, 4) or k_cache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("expected q [B,Hq,D] or [B,T,Hq,D], caches [num_blocks,16,Hkv,D], "
+                         "block_table [B,max_blocks]")
     single = q.dim() == 3
     q4 = q[:, None] if single else q
     B, T, Hq, D = q4.shape
     nblocks, bs, Hkv, Dk = k_cache.shape
     if Dk != D or v_cache.shape != k_cache.shape or block_table.shape[0] != B or ctx_lens.shape != (B,):
         raise ValueError("inconsistent decode shapes")
+    _check_out(out, q.shape, torch.bfloat16, "out")
+    _check_out(lse_out, (B, Hq) if single else (B, Hq, T), torch.float32, "lse_out")
+    _check_workspace(workspace)
+    _need_gpu(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out, workspace)
+    _same_device(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out, workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if workspace is None:
@@ -219,15 +268,21 @@ def decode_paged(q, k_cache, v_cache, block_table, ctx_lens, num_splits: int = 0
     int32; ctx_lens [B] int32.  Returns (o [B,Hq,D] bf16, lse [B,Hq] fp32 or None)."""
     import torch
     lib = _lib.load()
-    _need_gpu(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out, workspace)
     if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
         raise TypeError("decode_paged takes bf16 q and caches")
     if block_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
         raise TypeError("block_table and ctx_lens must be int32")
+    if q.dim() != 3 or k_cache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("expected q [B,Hq,D], caches [num_blocks,16,Hkv,D], block_table [B,max_blocks]")
     B, Hq, D = q.shape
     nblocks, bs, Hkv, Dk = k_cache.shape
     if Dk != D or v_cache.shape != k_cache.shape or block_table.shape[0] != B or ctx_lens.shape != (B,):
         raise ValueError("inconsistent decode shapes")
+    _check_out(out, q.shape, torch.bfloat16, "out")
+    _check_out(lse_out, (B, Hq), torch.float32, "lse_out")
+    _check_workspace(workspace)
+    _need_gpu(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out, workspace)
+    _same_device(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out, workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     max_blocks = block_table.shape[1]
@@ -245,3 +300,4 @@ def decode_paged(q, k_cache, v_cache, block_table, ctx_lens, num_splits: int = 0
     if st != _lib.ATTN_OK:
         raise AttnError(st, "attn_decode_paged")
     return o, lse
+

@@ -14,6 +14,8 @@ at the bf16 MFMA peak plus decode KV bytes at the HBM peak) over its measured
 time, in percent; the per-part absolute rates are in `parts`.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --split-sweep      (Flash-Decoding split threshold sweep, one JSON line)
+       python bench.py --compare-sdpa     (PyTorch's fused attention beside attn_prefill)
 """
 from __future__ import annotations
 
@@ -33,7 +35,7 @@ PEAK_HBM_BPS = 8.0e12         # MI355X HBM3E
 COPY_BYTES = 1 << 30          # calibration copy (profiling runs only)
 # Workloads beyond the hot path's step, timed on their own after it (never
 # part of `value` or `ms_per_step`).
-EXTRAS = ("chunked_prefill", "decode_multi", "decode_b64_fp8")
+EXTRAS = ("prefill_2k", "chunked_prefill", "decode_multi", "decode_b64_fp8")
 FP8_SCALE = 1.0 / 32          # per-tensor K and V scale of the fp8 extra
 MULTI_T = 4                   # new tokens per sequence in the multi-token decode extra
 METRIC = "prefill attn TFLOP/s + decode KV GB/s, % of MI355X bf16/HBM peak"
@@ -48,6 +50,10 @@ def parse():
     p.add_argument("--parts", default="prefill,decode_b64,decode_128k," + ",".join(EXTRAS),
                    help="comma-separated subset (for profiling runs); 'copy' adds a plain "
                         "1 GiB device-to-device copy that calibrates the HBM byte counters")
+    p.add_argument("--split-sweep", action="store_true",
+                   help="instead of the benchmark, sweep paged decode over context lengths and "
+                        "batch sizes with one chunk (Flash-Decoding off), the library's automatic "
+                        "count and every explicit count; one JSON line")
     p.add_argument("--compare-sdpa", action="store_true",
                    help="instead of the benchmark, time PyTorch's fused attention (SDPA, flash "
                         "backend) beside attn_prefill on the prefill workload; one JSON line")
@@ -107,6 +113,103 @@ def compare_sdpa(steps, warmup):
                       "sdpa_ms": sdpa_ms, "sdpa_tflops": flops / sdpa_ms / 1e9,
                       "speedup": sdpa_ms / ours_ms,
                       "max_abs_diff": (o_sdpa.float() - o_ours.float()).abs().max().item()}))
+
+
+def stats(ms_list):
+    """Mean, median and minimum of per-call event times (ms)."""
+    xs = sorted(ms_list)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return {"ms": sum(xs) / n, "ms_median": med, "ms_min": xs[0]}
+
+
+SWEEP_CTX = (256, 512, 1024, 2048, 4096, 8192, 16384, 32768, 131072)
+SWEEP_BATCH = (1, 4, 16, 64)
+SWEEP_THRESHOLDS = (256, 512, 1024, 2048, 4096)
+
+
+def split_sweep(reps):
+    """Flash-Decoding threshold sweep ("GPU Kernel 调度：大模型推理的拐点 2026",
+    checklist item 2 and advice 2: measure decode latency with the split
+    enabled and disabled over sequence lengths, find the knee, and check that
+    where splitting applies it is at least 30% faster).
+
+    Workload: bf16 paged decode, 32 query / 8 KV heads, head_dim 128, equal
+    context lengths per batch, shuffled 16-token blocks.  For each (context,
+    batch): one chunk (splitting off), the library's automatic count, and
+    every power-of-two count up to 256 (chunks of at least 16 tokens); the
+    median of `reps` event-timed calls each, interleaved over three rounds
+    (best round kept).  Batch 64 at 131072 tokens (34 GB of cache) is left
+    out; the other shapes fit with room to spare."""
+    import torch
+
+    import attention_flash_fwd_amd as afa
+    from attention_flash_fwd_amd import _lib, inputs
+
+    _lib.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    Hq, Hkv, D = 32, 8, 128
+    rows = []
+    for L in SWEEP_CTX:
+        for B in SWEEP_BATCH:
+            if L * B > 32768 * 64:
+                continue
+            inp = inputs.decode_inputs([L] * B, Hq, Hkv, D, seed=L + B, device=dev)
+            counts = [1] + [c for c in (2, 4, 8, 16, 32, 64, 128, 256) if (L + c - 1) // c >= 16]
+            auto = afa.decode_num_splits(B, Hkv, inp.block_table.shape[1], 16, 0)
+            o = torch.empty_like(inp.q)
+            lse = torch.empty(inp.q.shape[:2], dtype=torch.float32, device=dev)
+            wss = {c: afa.decode_workspace(inp.q, inp.k_cache, inp.block_table, c)
+                   for c in set(counts + [auto])}
+
+            def call(c):
+                afa.decode_paged(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                 num_splits=c, out=o, lse_out=lse, workspace=wss[c])
+
+            best = {c: float("inf") for c in wss}
+            for _ in range(3):
+                for c in wss:
+                    for _ in range(3):
+                        call(c)
+                    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                           for _ in range(reps)]
+                    for a_ev, b_ev in evs:
+                        a_ev.record(stream)
+                        call(c)
+                        b_ev.record(stream)
+                    torch.cuda.synchronize()
+                    best[c] = min(best[c], stats([a_ev.elapsed_time(b_ev) for a_ev, b_ev in evs])["ms_median"])
+            c_best = min(best, key=best.get)
+            row = {"ctx": L, "batch": B, "off_us": best[1] * 1e3, "auto_splits": auto,
+                   "auto_us": best[auto] * 1e3, "best_splits": c_best, "best_us": best[c_best] * 1e3,
+                   "auto_vs_best": best[auto] / best[c_best], "auto_speedup_vs_off": best[1] / best[auto],
+                   "by_splits_us": {str(c): best[c] * 1e3 for c in sorted(best)}}
+            rows.append(row)
+            print(f"sweep ctx {L} batch {B}: off {row['off_us']:.1f} us, auto({auto}) {row['auto_us']:.1f} us, "
+                  f"best({c_best}) {row['best_us']:.1f} us", file=sys.stderr, flush=True)
+            del inp, wss, o, lse
+            torch.cuda.empty_cache()
+    # The page's threshold policy: split (at the library's count) only when
+    # the context reaches the threshold, else one chunk.
+    policy = {}
+    for t in SWEEP_THRESHOLDS:
+        tot = sum((r["auto_us"] if r["ctx"] >= t else r["off_us"]) for r in rows)
+        policy[str(t)] = {"sum_us_over_shapes": tot}
+    tot_auto = sum(r["auto_us"] for r in rows)
+    # Where splitting applies (the library picks more than one chunk), how
+    # much faster than one chunk is it?
+    split_rows = [r for r in rows if r["auto_splits"] > 1]
+    print(json.dumps({
+        "sweep": "flash_decoding_split_threshold",
+        "workload": "paged_decode_h32kv8_d128_bf16, equal contexts per batch",
+        "reps": reps, "rows": rows, "threshold_policy": policy,
+        "library_policy_sum_us": tot_auto,
+        "auto_within_5pct_of_best": sum(1 for r in rows if r["auto_vs_best"] <= 1.05),
+        "shapes": len(rows),
+        "split_shapes_30pct_faster_than_off": sum(1 for r in split_rows if r["auto_speedup_vs_off"] >= 1 / 0.7),
+        "split_shapes": len(split_rows),
+    }), flush=True)
 
 
 def decode_bytes(inp, n_q_heads):
@@ -218,6 +321,9 @@ def main():
     if args.compare_sdpa:
         compare_sdpa(args.steps, args.warmup)
         return
+    if args.split_sweep:
+        split_sweep(reps=max(5, min(args.steps, 50)))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path).", file=sys.stderr)
@@ -245,6 +351,12 @@ def main():
         lse = torch.empty(inp.q.shape[:2], dtype=torch.float32, device=dev)
         dec[name] = (cfg, inp, ws, o, lse)
     extra_in = {}
+    if "prefill_2k" in parts:
+        p2 = inputs.PREFILL_2K
+        q2, k2, v2 = inputs.prefill_config_inputs(p2, device=dev)
+        o2 = torch.empty_like(q2)
+        l2 = torch.empty((p2.batch, p2.n_q_heads, p2.seqlen), dtype=torch.float32, device=dev)
+        extra_in["prefill_2k"] = (p2, q2, k2, v2, o2, l2)
     if "chunked_prefill" in parts:
         cp = inputs.CHUNKED_PREFILL
         cinp = inputs.decode_inputs([cp.ctx] * cp.batch, cp.n_q_heads, cp.n_kv_heads, cp.head_dim,
@@ -311,7 +423,13 @@ def main():
                              FP8_SCALE, FP8_SCALE, num_splits=fcfg.num_splits, scale=fcfg.scale, out=fo,
                              lse_out=flse, workspace=fws)
 
+    def run_prefill_2k():
+        p2, q2, k2, v2, o2, l2 = extra_in["prefill_2k"]
+        afa.prefill(q2, k2, v2, causal=True, scale=p2.scale, out=o2, lse_out=l2)
+
     extra_runners = []
+    if "prefill_2k" in extra_in:
+        extra_runners.append(("prefill_2k", run_prefill_2k))
     if "decode_b64_fp8" in extra_in:
         extra_runners.append(("decode_b64_fp8", run_fp8))
     if "chunked_prefill" in extra_in:
@@ -345,7 +463,8 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
 
-    part_ms = {name: sum(a.elapsed_time(b) for a, b in ev[name]) / args.steps for name, _ in runners}
+    part_stats = {name: stats([a.elapsed_time(b) for a, b in ev[name]]) for name, _ in runners}
+    part_ms = {name: st["ms"] for name, st in part_stats.items()}
 
     # ---- extras: timed on their own, after the step ----------------------
     extras = {}
@@ -358,11 +477,18 @@ def main():
             fn()
             b_ev.record(stream)
         torch.cuda.synchronize()
-        ms = sum(a_ev.elapsed_time(b_ev) for a_ev, b_ev in evs) / args.steps
-        if name == "chunked_prefill":
+        st = stats([a_ev.elapsed_time(b_ev) for a_ev, b_ev in evs])
+        ms = st["ms"]
+        if name == "prefill_2k":
+            p2 = extra_in[name][0]
+            tf = p2.flops() / (ms * 1e-3) / 1e12
+            extras[name] = {"workload": p2.name, **st, "tflops": tf,
+                            "frac_of_peak": tf * 1e12 / PEAK_BF16_FLOPS, "flops": p2.flops(),
+                            "tflops_at_median": p2.flops() / (st["ms_median"] * 1e-3) / 1e12}
+        elif name == "chunked_prefill":
             cp = extra_in[name][0]
             tf = cp.flops() / (ms * 1e-3) / 1e12
-            extras[name] = {"workload": cp.name, "ms": ms, "tflops": tf,
+            extras[name] = {"workload": cp.name, **st, "tflops": tf,
                             "frac_of_peak": tf * 1e12 / PEAK_BF16_FLOPS, "flops": cp.flops()}
         elif name == "decode_b64_fp8":
             fcfg, finp = extra_in[name][:2]
@@ -371,7 +497,7 @@ def main():
             nb = (inputs.decode_kv_bytes(finp.ctx, finp.n_kv_heads, D, elem_bytes=1) + 2 * B * Hq * D * 2
                   + used_blocks * 4 + B * 4)
             gbps = nb / (ms * 1e-3) / 1e9
-            extras[name] = {"workload": fcfg.name.replace("bf16", "fp8kv"), "ms": ms, "gbps": gbps,
+            extras[name] = {"workload": fcfg.name.replace("bf16", "fp8kv"), **st, "gbps": gbps,
                             "frac_of_peak": gbps * 1e9 / PEAK_HBM_BPS, "bytes": nb,
                             "num_splits": fcfg.num_splits, "kv_format": "e4m3, per-tensor scale"}
         elif name == "decode_multi":
@@ -381,7 +507,7 @@ def main():
             # the library's split count, read back from its workspace size (fp32 partial
             # outputs and log-sum-exps per (sequence, token, query head, split), 256-byte aligned)
             splits = mws.numel() // (mq.shape[0] * mq.shape[1] * mq.shape[2] * (mq.shape[3] + 1) * 4)
-            extras[name] = {"workload": f"{mcfg.name}_T{MULTI_T}", "ms": ms, "gbps": gbps,
+            extras[name] = {"workload": f"{mcfg.name}_T{MULTI_T}", **st, "gbps": gbps,
                             "frac_of_peak": gbps * 1e9 / PEAK_HBM_BPS, "bytes": nb,
                             "num_splits": int(splits)}
     out_parts = {}
@@ -390,13 +516,14 @@ def main():
         fl = pf_cfg.flops()
         tf = fl / (part_ms["prefill"] * 1e-3) / 1e12
         sol_ms += fl / PEAK_BF16_FLOPS * 1e3
-        out_parts["prefill"] = {"workload": pf_cfg.name, "ms": part_ms["prefill"], "tflops": tf,
-                                "frac_of_peak": tf * 1e12 / PEAK_BF16_FLOPS, "flops": fl}
+        out_parts["prefill"] = {"workload": pf_cfg.name, **part_stats["prefill"], "tflops": tf,
+                                "frac_of_peak": tf * 1e12 / PEAK_BF16_FLOPS, "flops": fl,
+                                "tflops_at_median": fl / (part_stats["prefill"]["ms_median"] * 1e-3) / 1e12}
     for name, (cfg, inp, ws, o, lse) in dec.items():
         nb = decode_bytes(inp, cfg.n_q_heads)
         gbps = nb / (part_ms[name] * 1e-3) / 1e9
         sol_ms += nb / PEAK_HBM_BPS * 1e3
-        out_parts[name] = {"workload": cfg.name, "ms": part_ms[name], "gbps": gbps,
+        out_parts[name] = {"workload": cfg.name, **part_stats[name], "gbps": gbps,
                            "frac_of_peak": gbps * 1e9 / PEAK_HBM_BPS, "bytes": nb,
                            "num_splits": cfg.num_splits, "sum_ctx": sum(inp.ctx)}
     if "copy" in part_ms:

@@ -168,7 +168,11 @@ int attn_decode_num_splits(int batch, int n_kv_heads, int max_blocks_per_seq,
 
 /*
  * attn_decode_workspace_bytes -- size of the scratch buffer attn_decode_paged
- * needs for these arguments: the per-chunk partial outputs
+ * needs for these arguments.  It holds what Flash-Decoding keeps between its
+ * two kernels ("GPU Kernel 调度：大模型推理的拐点 2026", paragraphs on Flash
+ * Decoding and its cost: each chunk's partial output with its log-sum-exp,
+ * kept in fp32 because fp16 partials lose accuracy as the chunk count
+ * grows): the per-chunk partial outputs
  * [batch, n_q_heads, splits, head_dim] fp32 followed by their log-sum-exps
  * [batch, n_q_heads, splits] fp32 (splits = attn_decode_num_splits(...)),
  * then 256 bytes of scheduling state (a work counter, set by each call
@@ -193,7 +197,8 @@ size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
  *   o            [batch, n_q_heads, head_dim] bf16, written
  *   lse          [batch, n_q_heads] fp32, written; may be NULL
  *   workspace    device scratch of at least attn_decode_workspace_bytes(...)
- *                bytes, 256-byte aligned; its contents on entry do not
+ *                bytes, 16-byte aligned (ATTN_ERR_ALIGN otherwise; torch
+ *                allocations are 256-byte aligned); its contents on entry do not
  *                matter.  Calls that overlap in time (on different streams)
  *                need workspaces of their own.
  *
@@ -237,7 +242,7 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
  *   q            [batch, seqlen_q, n_q_heads, head_dim]             bf16
  *   o            [batch, seqlen_q, n_q_heads, head_dim]             bf16, written
  *   lse          [batch, n_q_heads, seqlen_q] fp32, written; may be NULL
- *   workspace    attn_decode_multi_workspace_bytes(...) bytes, 256-byte aligned
+ *   workspace    attn_decode_multi_workspace_bytes(...) bytes, 16-byte aligned
  *   other arguments as for attn_decode_paged.
  *
  * Token t (0-based) of sequence b sits at position ctx_lens[b] - seqlen_q + t
@@ -309,7 +314,9 @@ size_t attn_decode_multi_workspace_bytes(int batch, int seqlen_q, int n_q_heads,
                                          int head_dim, int max_blocks_per_seq, int block_size,
                                          int num_splits);
 
-/* Human-readable name of a status code (static storage, never NULL). */
+/* Human-readable name of a status code (static storage, never NULL).  Part
+ * of the boundary's plumbing: the pages define no error model, so the codes
+ * and their names are this library's own. */
 const char *attn_status_string(attn_status_t status);
 
 /* ABI version of this header: (major << 16) | minor. */

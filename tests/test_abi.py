@@ -270,6 +270,52 @@ def test_binding_rejects_cpu_tensors():
         afa.prefill(q, q[:, :, :1].contiguous(), q[:, :, :1].contiguous())
 
 
+def test_binding_rejects_wrong_outputs_before_any_launch():
+    # A caller-supplied out / lse_out of the wrong shape or dtype would let
+    # the kernels write past it (the C ABI only sees a pointer).  The binding
+    # refuses it before any device check or library call, so CPU tensors
+    # reach these checks here.
+    import torch
+    import attention_flash_fwd_amd as afa
+    bf, f32 = torch.bfloat16, torch.float32
+    q = torch.zeros(2, 8, 4, 64, dtype=bf)
+    k = torch.zeros(2, 8, 2, 64, dtype=bf)
+    bad_prefill = [
+        dict(out=torch.zeros(2, 8, 4, 32, dtype=bf)),            # too small
+        dict(out=torch.zeros(2, 8, 4, 64, dtype=f32)),           # fp32 out for bf16 q
+        dict(lse_out=torch.zeros(2, 8, 4, dtype=f32)),           # [B,Sq,Hq] instead of [B,Hq,Sq]
+        dict(lse_out=torch.zeros(2, 4, 8, dtype=bf)),            # lse must be fp32
+        dict(out=torch.zeros(2, 4, 8, 64, dtype=bf).transpose(1, 2)),   # not contiguous
+    ]
+    for kw in bad_prefill:
+        with pytest.raises(ValueError, match="out"):
+            afa.prefill(q, k, k.clone(), **kw)
+    # Paged entry points: q of one token [B,Hq,D] / several [B,T,Hq,D].
+    kc = torch.zeros(4, 16, 2, 64, dtype=bf)
+    tbl = torch.zeros(2, 2, dtype=torch.int32)
+    ctx = torch.zeros(2, dtype=torch.int32)
+    q1 = torch.zeros(2, 4, 64, dtype=bf)
+    q3 = torch.zeros(2, 3, 4, 64, dtype=bf)
+    with pytest.raises(ValueError, match="out"):
+        afa.decode_paged(q1, kc, kc.clone(), tbl, ctx, out=torch.zeros(2, 4, 32, dtype=bf))
+    with pytest.raises(ValueError, match="lse_out"):
+        afa.decode_paged(q1, kc, kc.clone(), tbl, ctx, lse_out=torch.zeros(2, 4, 1, dtype=f32))
+    with pytest.raises(ValueError, match="lse_out"):
+        afa.decode_paged_multi(q3, kc, kc.clone(), tbl, ctx, lse_out=torch.zeros(2, 3, 4, dtype=f32))
+    with pytest.raises(ValueError, match="out"):
+        afa.decode_paged_multi(q3, kc, kc.clone(), tbl, ctx, out=torch.zeros(2, 3, 4, 64, dtype=f32))
+    with pytest.raises(ValueError, match="out"):
+        afa.prefill_paged(q3, kc, kc.clone(), tbl, ctx, out=torch.zeros(2, 3, 4, 63, dtype=bf))
+    k8 = torch.zeros(4, 16, 2, 64, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="lse_out"):
+        afa.decode_paged_fp8(q1, k8, k8.clone(), tbl, ctx, 1.0, 1.0, lse_out=torch.zeros(2, 4, 1, dtype=f32))
+    with pytest.raises(ValueError, match="workspace"):
+        afa.decode_paged(q1, kc, kc.clone(), tbl, ctx, workspace=torch.zeros(64, dtype=torch.float32))
+    # Correct outputs pass these checks and reach the device check.
+    with pytest.raises(ValueError, match="GPU only"):
+        afa.prefill(q, k, k.clone(), out=torch.empty_like(q), lse_out=torch.zeros(2, 4, 8, dtype=f32))
+
+
 def test_every_kernel_launch_stub_is_defined():
     # A kernel whose body the host pass cannot compile (for example a device
     # builtin called directly from a lambda) silently loses its launch stub;

@@ -409,6 +409,17 @@ def test_decode_matches_last_row_of_causal_prefill(afa):
     assert (lp[0, :, L - 1] - ld[0]).abs().max().item() <= 1e-4
 
 
+def sample_sequences(ctx, nseq, seed):
+    """nseq sequence ids (at most all of them): always the longest and the
+    shortest, then seeded random others; sorted only after the choice."""
+    ctx = np.asarray(ctx)
+    must = [int(np.argmax(ctx)), int(np.argmin(ctx))]
+    rng = np.random.default_rng(seed)
+    others = [int(x) for x in rng.permutation(len(ctx)) if int(x) not in must]
+    chosen = list(dict.fromkeys(must)) + others
+    return sorted(chosen[:max(nseq, len(set(must)))])
+
+
 @pytest.mark.parametrize("cfg_name,nseq", [("paged_decode_b64_h32kv8_d128_ctx512-32768_bf16", 8),
                                            ("paged_decode_b4_h64kv8_d128_ctx131072_bf16", 2)])
 def test_decode_full_size_sampled(afa, cfg_name, nseq):
@@ -418,10 +429,7 @@ def test_decode_full_size_sampled(afa, cfg_name, nseq):
     inp = inputs.decode_config_inputs(cfg, device="cuda")
     o, lse = run_decode(afa, inp, cfg.num_splits)
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
-    rng = np.random.default_rng(77)
-    ctx = np.array(inp.ctx)
-    seqs = sorted(set([int(np.argmax(ctx)), int(np.argmin(ctx))] +
-                      [int(x) for x in rng.choice(len(ctx), size=nseq, replace=False)]))[:max(nseq, 2)]
+    seqs = sample_sequences(inp.ctx, nseq, seed=77)
     o_ref, l_ref = decode_oracle(inp, cfg.scale, seqs)
     check_o(to_np(o)[seqs], o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
     check_lse(to_np(lse)[seqs], l_ref, BF16_LSE_ABS)
@@ -654,3 +662,132 @@ def test_decode_fp8_permutation_and_nan_contract(afa):
     torch.cuda.synchronize()
     assert torch.isnan(o_c[1]).all() and torch.isnan(l_c[1]).all()
     assert torch.equal(o_c[0], o_a[0]) and torch.equal(o_c[2], o_a[2])
+
+
+# --------------------------------------- benchmark workloads beyond the step ---
+# The benchmark times two more decode workloads on the batch-64 cache shape:
+# an e4m3 copy of the cache (scale 1/32, 16 chunks) and four new tokens per
+# sequence (the library's split count).  Both are checked here at that size,
+# in the same launch configuration, on sampled sequences.
+BENCH_FP8_SCALE = 1.0 / 32
+BENCH_MULTI_T = 4
+
+
+def test_decode_fp8_benchmark_workload_sampled(afa):
+    from attention_flash_fwd_amd import inputs
+    cfg = inputs.DECODE_B64
+    say(f"case {cfg.name} fp8 e4m3 cache, scale 1/32, {cfg.num_splits} splits (sampled sequences)")
+    ctx = inputs.decode_context_lengths(cfg.batch, cfg.ctx_min, cfg.ctx_max, cfg.seed)
+    inp = inputs.decode_inputs(ctx, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seed, "cuda",
+                               kv_format="fp8", k_scale=BENCH_FP8_SCALE, v_scale=BENCH_FP8_SCALE)
+    o, lse = afa.decode_paged_fp8(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                  BENCH_FP8_SCALE, BENCH_FP8_SCALE, num_splits=cfg.num_splits,
+                                  scale=cfg.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    seqs = sample_sequences(ctx, 8, seed=78)
+    assert int(np.argmax(ctx)) in seqs and int(np.argmin(ctx)) in seqs
+    o_ref, l_ref = fp8_oracle(inp, inp.q, cfg.scale, seqs)
+    check_o(to_np(o)[seqs], o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse)[seqs], l_ref, BF16_LSE_ABS)
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_decode_multi_benchmark_workload_sampled(afa):
+    from attention_flash_fwd_amd import inputs
+    cfg = inputs.DECODE_B64
+    say(f"case {cfg.name} T={BENCH_MULTI_T}, library split count (sampled sequences)")
+    inp = inputs.decode_config_inputs(cfg, device="cuda")
+    q = inputs.chunk_queries(cfg.batch, BENCH_MULTI_T, cfg.n_q_heads, cfg.head_dim, seed=cfg.seed,
+                             device="cuda")
+    ws = afa.decode_workspace(q, inp.k_cache, inp.block_table, 0)
+    o, lse = afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                    num_splits=0, scale=cfg.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    seqs = sample_sequences(inp.ctx, 8, seed=79)
+    o_ref, l_ref = paged_prefill_oracle(inp, q, True, cfg.scale, seqs=seqs)
+    check_o(to_np(o)[seqs], o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse)[seqs], l_ref, BF16_LSE_ABS)
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_decode_fp8_every_finite_code(afa):
+    # Every finite e4m3 code (254 of 256; 0x7F and 0xFF are NaN) sits in the
+    # cache of a one-token sequence, as a K element and as a V element.  With
+    # one visible key P = 1 exactly, so O is that V row widened to bf16
+    # (exact: every e4m3 value is a bf16 value) and must equal the oracle's
+    # decoding bit for bit.  Query head h is the unit vector e_h and the score
+    # scale is 1, so lse of head h is the widened K element h times k_scale.
+    from attention_flash_fwd_amd import inputs
+    say("case decode_fp8 every finite e4m3 code (V exact, K through lse)")
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    D, Hq, Hkv, B = 128, 128, 1, 2
+    codes = np.stack([finite[(b * D + np.arange(D)) % finite.size] for b in range(B)])    # [B, D]
+    assert set(codes.ravel().tolist()) == set(finite.tolist())
+    inp = inputs.decode_inputs([1] * B, Hq, Hkv, D, seed=3, device="cuda", spare_blocks=1,
+                               kv_format="fp8", k_scale=1.0, v_scale=1.0)
+    for b in range(B):
+        blk = int(inp.block_table[b, 0])
+        row = torch.from_numpy(codes[b]).cuda()
+        inp.k_cache[blk, 0, 0] = row
+        inp.v_cache[blk, 0, 0] = row
+    q = torch.eye(D, dtype=torch.bfloat16, device="cuda")[None].expand(B, Hq, D).contiguous()
+    for ks in (1.0, 0.5):
+        o, lse = afa.decode_paged_fp8(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                      ks, 1.0, num_splits=1, scale=1.0)
+        torch.cuda.synchronize()
+        want_v = oracle.e4m3_decode(codes)                                   # [B, D] float64
+        got = to_np(o).astype(np.float64)                                    # [B, Hq, D]
+        assert np.array_equal(got, np.broadcast_to(want_v[:, None, :], got.shape)), \
+            report_mismatch(got[:, 0], want_v)
+        want_l = want_v * ks                                                 # head h sees K element h
+        np.testing.assert_allclose(to_np(lse).astype(np.float64), want_l, rtol=2e-6, atol=1e-30)
+        # the same against the fp8 oracle entry point
+        kv = [(codes[b][None, None, :], codes[b][None, None, :]) for b in range(B)]
+        o_ref, l_ref = oracle.decode_fp8(to_np(q), [x[0] for x in kv], [x[1] for x in kv], 1.0, ks, 1.0)
+        assert np.array_equal(got, o_ref)
+        np.testing.assert_allclose(to_np(lse), l_ref, rtol=2e-6)
+
+
+def report_mismatch(got, want):
+    bad = np.argwhere(got != want)
+    return f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
+
+
+def test_prefill_batch_and_head_permutation(afa):
+    # Batch entries and KV-head groups are independent: permuting them in the
+    # input permutes the output, bit for bit (same kernel arithmetic per row).
+    say("case prefill batch / head-group permutation")
+    B, S, Hq, Hkv, D = 3, 300, 8, 4, 128
+    G = Hq // Hkv
+    q, k, v = gen_prefill(B, S, S, Hq, Hkv, D, torch.bfloat16, 404)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    o, lse = afa.prefill(q, k, v, causal=True)
+    bp = torch.tensor([2, 0, 1], device="cuda")
+    kp = torch.tensor([3, 1, 0, 2], device="cuda")
+    qp = torch.stack([torch.arange(G, device="cuda") + G * int(h) for h in kp]).reshape(-1)
+    o2, lse2 = afa.prefill(q[bp][:, :, qp].contiguous(), k[bp][:, :, kp].contiguous(),
+                           v[bp][:, :, kp].contiguous(), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o[bp][:, :, qp]) and torch.equal(lse2, lse[bp][:, qp])
+
+
+def test_decode_batch_and_head_permutation(afa):
+    # Same for paged decode: permuting the sequences (with their table rows
+    # and lengths) and the KV-head groups permutes the output bit for bit.
+    say("case decode batch / head-group permutation")
+    Hq, Hkv, D = 16, 4, 128
+    G = Hq // Hkv
+    inp = gen_decode([700, 33, 2100, 16], Hq, Hkv, D, seed=405)
+    o, lse = run_decode(afa, inp, 4)
+    bp = torch.tensor([3, 0, 2, 1], device="cuda")
+    kp = torch.tensor([2, 0, 3, 1], device="cuda")
+    qp = torch.stack([torch.arange(G, device="cuda") + G * int(h) for h in kp]).reshape(-1)
+    o2, lse2 = afa.decode_paged(inp.q[bp][:, qp].contiguous(), inp.k_cache[:, :, kp].contiguous(),
+                                inp.v_cache[:, :, kp].contiguous(), inp.block_table[bp].contiguous(),
+                                inp.ctx_lens[bp].contiguous(), num_splits=4)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o[bp][:, qp]) and torch.equal(lse2, lse[bp][:, qp])
