@@ -17,7 +17,7 @@ from . import _lib
 from ._lib import AttnError, MAX_SPLITS  # noqa: F401
 
 __all__ = ["prefill", "prefill_paged", "decode_paged", "decode_paged_multi", "decode_paged_fp8",
-           "decode_num_splits", "decode_workspace_bytes",
+           "decode_paged_noalloc", "decode_num_splits", "decode_workspace_bytes",
            "decode_workspace", "AttnError", "library_path"]
 
 
@@ -301,3 +301,40 @@ def decode_paged(q, k_cache, v_cache, block_table, ctx_lens, num_splits: int = 0
         raise AttnError(st, "attn_decode_paged")
     return o, lse
 
+
+def decode_paged_noalloc(q, k_cache, v_cache, block_table, ctx_lens, num_splits: int = 0,
+                         scale: float | None = None, out=None, lse_out=None, return_lse: bool = True):
+    """decode_paged without a workspace: the library uses its own device
+    array (attn_decode_paged_noalloc; the call itself allocates nothing, so
+    pass `out` and `lse_out` to allocate nothing here either).  Calls that
+    overlap in time on one GPU share that array and race.  Raises AttnError
+    (ATTN_ERR_WORKSPACE) when the shape needs more than the array holds."""
+    import torch
+    lib = _lib.load()
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise TypeError("decode_paged_noalloc takes bf16 q and caches")
+    if block_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
+        raise TypeError("block_table and ctx_lens must be int32")
+    if q.dim() != 3 or k_cache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("expected q [B,Hq,D], caches [num_blocks,16,Hkv,D], block_table [B,max_blocks]")
+    B, Hq, D = q.shape
+    nblocks, bs, Hkv, Dk = k_cache.shape
+    if Dk != D or v_cache.shape != k_cache.shape or block_table.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("inconsistent decode shapes")
+    _check_out(out, q.shape, torch.bfloat16, "out")
+    _check_out(lse_out, (B, Hq), torch.float32, "lse_out")
+    _need_gpu(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out)
+    _same_device(q, k_cache, v_cache, block_table, ctx_lens, out, lse_out)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = out if out is not None else torch.empty_like(q)
+    lse = lse_out
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = lib.attn_decode_paged_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                       _ptr(ctx_lens), _ptr(o), _ptr(lse), B, Hq, Hkv, D, nblocks, bs,
+                                       block_table.shape[1], int(num_splits), float(scale),
+                                       _stream_handle(q))
+    if st != _lib.ATTN_OK:
+        raise AttnError(st, "attn_decode_paged_noalloc")
+    return o, lse

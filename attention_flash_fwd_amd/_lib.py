@@ -21,10 +21,11 @@ STATUS_NAMES = {
 ATTN_BF16 = 0
 ATTN_F32 = 1
 MAX_SPLITS = 256
+STATIC_SCRATCH_BYTES = 32 << 20     # ATTN_STATIC_SCRATCH_BYTES
 
 # Every symbol include/attn.h declares.
 EXPORTED = ("attn_prefill", "attn_prefill_paged", "attn_decode_paged", "attn_decode_paged_multi",
-            "attn_decode_paged_fp8",
+            "attn_decode_paged_fp8", "attn_decode_paged_noalloc",
             "attn_decode_workspace_bytes", "attn_decode_multi_workspace_bytes",
             "attn_decode_num_splits", "attn_status_string", "attn_abi_version")
 
@@ -48,6 +49,8 @@ def _declare(lib):
     lib.attn_prefill_paged.restype = I
     lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, Z, P]
     lib.attn_decode_paged.restype = I
+    lib.attn_decode_paged_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+    lib.attn_decode_paged_noalloc.restype = I
     lib.attn_decode_paged_multi.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P, Z, P]
     lib.attn_decode_paged_multi.restype = I
     lib.attn_decode_paged_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, F, F, P, Z, P]

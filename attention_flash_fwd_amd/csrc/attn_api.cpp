@@ -365,4 +365,28 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
                                    stream);
 }
 
+attn_status_t attn_decode_paged_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                        const int32_t *block_table, const int32_t *ctx_lens,
+                                        void *o, float *lse,
+                                        int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                        int num_blocks, int block_size, int max_blocks_per_seq,
+                                        int num_splits, float scale, attn_stream_t stream)
+{
+    // The size check runs before anything touches the device.  A shape the
+    // workspace rules reject (0 bytes) goes on to decode_common, which
+    // returns the matching status code without launching.
+    const size_t need = attn_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
+                                                    max_blocks_per_seq, block_size, num_splits);
+    if (need > ATTN_STATIC_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0 && batch > 0) {
+        ws = attn::static_scratch();
+        if (ws == nullptr) return ATTN_ERR_LAUNCH;
+    }
+    return decode_common(q, k_cache, v_cache, block_table, ctx_lens, o, lse, batch, 1, n_q_heads,
+                         n_kv_heads, head_dim, num_blocks, block_size, max_blocks_per_seq, num_splits,
+                         scale, false, 1.0f, 1.0f, ws, ws != nullptr ? ATTN_STATIC_SCRATCH_BYTES : 0,
+                         stream);
+}
+
 }  // extern "C"

@@ -40,6 +40,8 @@
 //   With a single chunk the merge is the identity (w = 1), so the split
 //   kernel writes O and lse itself and this kernel is not launched.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "gfx950.hpp"
 #include "kernels.hpp"
@@ -726,6 +728,31 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
 }
 
 }  // namespace
+
+// Library-held decode workspace for callers that cannot allocate: one array
+// per GPU the library runs on, held until the process ends.  Host code never
+// uses the array's name as an address (on the host it is only a stand-in for
+// the symbol); it uses the device address that hipGetSymbolAddress returns,
+// looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[ATTN_STATIC_SCRATCH_BYTES];
+
+void *static_scratch()
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void *> ptrs[kMaxDevices];
+    static std::mutex mu;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = ptrs[dev].load(std::memory_order_acquire);
+    if (p != nullptr) return p;
+    std::lock_guard<std::mutex> lock(mu);
+    p = ptrs[dev].load(std::memory_order_relaxed);
+    if (p != nullptr) return p;
+    void *addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr) return nullptr;
+    ptrs[dev].store(addr, std::memory_order_release);
+    return addr;
+}
 
 hipError_t launch_decode(const DecodeArgs &a, int head_dim, bool kv_fp8, hipStream_t s)
 {

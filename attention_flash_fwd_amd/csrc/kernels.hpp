@@ -44,4 +44,9 @@ hipError_t launch_prefill_f32(const PrefillArgs &a, int head_dim, bool causal, h
 hipError_t launch_prefill_paged_bf16(const PrefillArgs &a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int head_dim, bool kv_fp8, hipStream_t s);
 
+// Device address of the library-held decode workspace of the current device
+// (ATTN_STATIC_SCRATCH_BYTES bytes; looked up once per device), or nullptr if
+// the lookup failed.
+void *static_scratch();
+
 }  // namespace attn

@@ -230,6 +230,41 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
                                 attn_stream_t stream);
 
 /*
+ * attn_decode_paged_noalloc -- attn_decode_paged without a caller-provided
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * arguments and results are those of attn_decode_paged with the workspace
+ * arguments removed; the same kernels run with the same split count, so the
+ * outputs are bit-identical to attn_decode_paged's.
+ *
+ * The workspace is a library-held array of ATTN_STATIC_SCRATCH_BYTES in
+ * device memory, one per GPU the library runs on, held until the process
+ * ends.  The call allocates nothing (no hipMalloc, no library allocator); the
+ * first call on a device looks the array's device address up once.  Nothing
+ * in the array has to start at zero: every partial is written before it is
+ * read, and the work counter is reset by the kernel itself.  Every call on a
+ * GPU shares that GPU's array and finds it as the last call left it, so calls
+ * that overlap in time on one GPU (different streams, or several host
+ * threads) RACE and give undefined results; serialise them, or use
+ * attn_decode_paged with a workspace each.
+ *
+ * Returns ATTN_ERR_WORKSPACE, without touching the device, when
+ * attn_decode_workspace_bytes(...) for these arguments exceeds
+ * ATTN_STATIC_SCRATCH_BYTES (32 MiB: batch 64 with 32 query heads at
+ * head_dim 128 fits up to 31 splits; batch 4 with 64 query heads and 64
+ * splits takes 8.4 MB); ATTN_ERR_LAUNCH if the array's
+ * address cannot be obtained; otherwise the codes of attn_decode_paged.
+ */
+#define ATTN_STATIC_SCRATCH_BYTES (32u << 20)
+
+attn_status_t attn_decode_paged_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                        const int32_t *block_table, const int32_t *ctx_lens,
+                                        void *o, float *lse,
+                                        int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                        int num_blocks, int block_size, int max_blocks_per_seq,
+                                        int num_splits, float scale, attn_stream_t stream);
+
+/*
  * attn_decode_paged_multi -- seqlen_q new query tokens per sequence over a
  * paged KV cache that already holds their keys: the verification step of
  * speculative decoding, where the draft tokens are checked in one pass
@@ -322,7 +357,7 @@ const char *attn_status_string(attn_status_t status);
 /* ABI version of this header: (major << 16) | minor. */
 int attn_abi_version(void);
 
-#define ATTN_ABI_VERSION ((1 << 16) | 4)
+#define ATTN_ABI_VERSION ((1 << 16) | 5)
 
 #ifdef __cplusplus
 }

@@ -59,7 +59,7 @@ def test_exports_are_c_symbols():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.attn_abi_version() == (1 << 16) | 4
+    assert lib.attn_abi_version() == (1 << 16) | 5
     for code in range(8):
         s = lib.attn_status_string(code).decode()
         assert s and s != "unknown status"
