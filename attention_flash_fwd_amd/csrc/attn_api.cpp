@@ -51,13 +51,22 @@ attn_status_t check_prefill(const void *q, const void *k, const void *v, const v
 // at 128K at 64; 32 sequences of 1024 tokens at one chunk, 24.5 us against
 // 37 us at the four that a 2048-item target gave.)
 constexpr long long kFillItems = 256;
+// Below this many tokens (the longest sequence the table can hold), one
+// chunk per sequence: the Flash-Decoding threshold of "GPU Kernel 调度：大模型
+// 推理的拐点 2026" (advice 2 and checklist item 2: below about 1024 tokens
+// splitting is slower than not splitting).  The split-count sweep on MI355X
+// (bench.py --split-sweep) agrees: at 512 tokens every split count is within
+// a microsecond of one chunk or slower (batch 16: 14.1 us with one chunk,
+// 15.9 us with two), while from 1024 tokens on, batches of 1-4 sequences
+// decode 33-39% faster split.
+constexpr long long kSplitThresholdTokens = 1024;
 
 int resolve_splits(int batch, int n_kv_heads, int max_blocks, int block_size, int num_splits)
 {
     if (num_splits >= 1) return num_splits <= ATTN_MAX_SPLITS ? num_splits : 0;
     const long long max_tokens = (long long)max_blocks * block_size;
     const long long units = (long long)batch * n_kv_heads;
-    if (units <= 0 || max_tokens <= 0) return 1;
+    if (units <= 0 || max_tokens < kSplitThresholdTokens) return 1;
     const long long by_length = (max_tokens + 2047) / 2048;
     // About one (chunk, sequence, KV head) item per compute unit: below
     // that, more chunks pay off; above it, each extra chunk costs more (its

@@ -157,11 +157,13 @@ attn_status_t attn_prefill_paged(const void *q, const void *k_cache, const void 
  * attn_decode_paged will use for these arguments.  num_splits >= 1 is
  * returned unchanged (after the range check of attn_decode_paged);
  * num_splits <= 0 asks for the library's choice, which depends only on the
- * arguments given here (never on device data): chunks of about 2048 tokens
- * of the longest sequence the table can hold, or more chunks (none shorter
- * than 256 tokens) when that is needed for about 256 (chunk, sequence, KV
- * head) items, one per compute unit, to occupy the GPU.  Returns 0 for
- * invalid arguments.
+ * arguments given here (never on device data): one chunk when the table
+ * holds fewer than 1024 tokens per sequence (the Flash-Decoding threshold of
+ * "GPU Kernel 调度：大模型推理的拐点 2026", advice 2: below it splitting is
+ * slower), else chunks of about 2048 tokens of the longest sequence the
+ * table can hold, or more chunks (none shorter than 256 tokens) when that is
+ * needed for about 256 (chunk, sequence, KV head) items, one per compute
+ * unit, to occupy the GPU.  Returns 0 for invalid arguments.
  */
 int attn_decode_num_splits(int batch, int n_kv_heads, int max_blocks_per_seq,
                            int block_size, int num_splits);
