@@ -50,6 +50,11 @@ def parse():
     p.add_argument("--parts", default="prefill,decode_b64,decode_128k," + ",".join(EXTRAS),
                    help="comma-separated subset (for profiling runs); 'copy' adds a plain "
                         "1 GiB device-to-device copy that calibrates the HBM byte counters")
+    p.add_argument("--multi-t", type=int, default=MULTI_T,
+                   help="new tokens per sequence of the decode_multi extra (profiling runs)")
+    p.add_argument("--multi-workload", choices=("b64", "128k"), default="b64",
+                   help="cache of the decode_multi extra: the batch-64 or the 128K-context decode "
+                        "workload (profiling runs)")
     p.add_argument("--split-sweep", action="store_true",
                    help="instead of the benchmark, sweep paged decode over context lengths and "
                         "batch sizes with one chunk (Flash-Decoding off), the library's automatic "
@@ -365,13 +370,14 @@ def main():
         co = torch.empty_like(cq)
         clse = torch.empty((cp.batch, cp.n_q_heads, cp.chunk), dtype=torch.float32, device=dev)
         extra_in["chunked_prefill"] = (cp, cinp, cq, co, clse)
+    multi_t = args.multi_t
     if "decode_multi" in parts:
-        mcfg = inputs.DECODE_B64
+        mcfg = inputs.DECODE_B64 if args.multi_workload == "b64" else inputs.DECODE_128K
         minp = inputs.decode_config_inputs(mcfg, device=dev)
-        mq = inputs.chunk_queries(mcfg.batch, MULTI_T, mcfg.n_q_heads, mcfg.head_dim, seed=mcfg.seed, device=dev)
+        mq = inputs.chunk_queries(mcfg.batch, multi_t, mcfg.n_q_heads, mcfg.head_dim, seed=mcfg.seed, device=dev)
         mws = afa.decode_workspace(mq, minp.k_cache, minp.block_table, 0)     # the library's split count
         mo = torch.empty_like(mq)
-        mlse = torch.empty((mcfg.batch, mcfg.n_q_heads, MULTI_T), dtype=torch.float32, device=dev)
+        mlse = torch.empty((mcfg.batch, mcfg.n_q_heads, multi_t), dtype=torch.float32, device=dev)
         extra_in["decode_multi"] = (mcfg, minp, mq, mws, mo, mlse)
     if "decode_b64_fp8" in parts:
         fcfg = inputs.DECODE_B64
@@ -502,12 +508,12 @@ def main():
                             "num_splits": fcfg.num_splits, "kv_format": "e4m3, per-tensor scale"}
         elif name == "decode_multi":
             mcfg, minp, mq, mws = extra_in[name][:4]
-            nb = decode_bytes(minp, mcfg.n_q_heads) + 2 * (MULTI_T - 1) * mq[:, 0].numel() * 2
+            nb = decode_bytes(minp, mcfg.n_q_heads) + 2 * (multi_t - 1) * mq[:, 0].numel() * 2
             gbps = nb / (ms * 1e-3) / 1e9
             # the library's split count, read back from its workspace size (fp32 partial
             # outputs and log-sum-exps per (sequence, token, query head, split), 256-byte aligned)
             splits = mws.numel() // (mq.shape[0] * mq.shape[1] * mq.shape[2] * (mq.shape[3] + 1) * 4)
-            extras[name] = {"workload": f"{mcfg.name}_T{MULTI_T}", **st, "gbps": gbps,
+            extras[name] = {"workload": f"{mcfg.name}_T{multi_t}", **st, "gbps": gbps,
                             "frac_of_peak": gbps * 1e9 / PEAK_HBM_BPS, "bytes": nb,
                             "num_splits": int(splits)}
     out_parts = {}
