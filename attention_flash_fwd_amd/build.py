@@ -14,7 +14,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libattn.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip"]
+SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "decode_wide.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -716,7 +716,8 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
     const long long n_grp = (n_ct + kMaxTiles - 1) / kMaxTiles;
     const long long nct = n_grp > 0 ? (n_ct + n_grp - 1) / n_grp : 1;
     hipError_t e;
-    if (nct <= 1) e = launch_split<D, EB, 1>(a, n_ct, s);
+    if (EB == 2 && n_ct > 2) e = launch_decode_wide(a, D, s);   // more than 32 columns, bf16 cache
+    else if (nct <= 1) e = launch_split<D, EB, 1>(a, n_ct, s);
     else if (nct == 2) e = launch_split<D, EB, 2>(a, n_ct, s);
     else if (nct == 3) e = launch_split<D, EB, 3>(a, n_ct, s);
     else e = launch_split<D, EB, kMaxTiles>(a, n_ct, s);

@@ -239,7 +239,8 @@ def source_digest(paths):
 KERNEL_SOURCES = {
     "prefill": ["attention_flash_fwd_amd/csrc/prefill_bf16.hip", "attention_flash_fwd_amd/csrc/gfx950.hpp",
                 "attention_flash_fwd_amd/csrc/kernels.hpp"],
-    "decode": ["attention_flash_fwd_amd/csrc/decode.hip", "attention_flash_fwd_amd/csrc/gfx950.hpp",
+    "decode": ["attention_flash_fwd_amd/csrc/decode.hip", "attention_flash_fwd_amd/csrc/decode_wide.hip",
+               "attention_flash_fwd_amd/csrc/gfx950.hpp",
                "attention_flash_fwd_amd/csrc/kernels.hpp"],
 }
 def sources_of(part):

@@ -791,3 +791,107 @@ def test_decode_batch_and_head_permutation(afa):
                                 inp.ctx_lens[bp].contiguous(), num_splits=4)
     torch.cuda.synchronize()
     assert torch.equal(o2, o[bp][:, qp]) and torch.equal(lse2, lse[bp][:, qp])
+
+
+# ------------------------------------- decode with more than 32 columns ---
+# More than 32 (token, head) columns over a bf16 cache take the wide split
+# kernel: 32 columns per wave, two or four waves per workgroup, 32-token
+# steps shared through LDS.  Cases: both workgroup widths, more than one
+# column group, D = 64, sign and size of the scale, the NaN contract, the
+# single-chunk direct write, and the 128K cache at the benchmark's size.
+@pytest.mark.parametrize("ctx,T,Hq,Hkv,D,splits,scale_mul,q_mul", [
+    ([700, 33, 1], 8, 64, 8, 128, 3, -1.0, 1.0),    # 64 columns, negative scale
+    ([700, 95], 16, 64, 8, 128, 2, 1.0, 16.0),      # 128 columns, large logits
+    ([400, 60], 8, 32, 4, 64, 2, 0.0, 1.0),         # D = 64, zero scale: uniform weights
+    ([250, 81], 20, 64, 8, 128, 4, 1.0, 1.0),       # 160 columns: two groups, the second one-quarter full
+])
+def test_decode_wide_scale_and_groups(afa, ctx, T, Hq, Hkv, D, splits, scale_mul, q_mul):
+    say(f"case decode wide ctx{ctx} T{T} Hq{Hq} Hkv{Hkv} D{D} splits{splits} scale x{scale_mul} q x{q_mul}")
+    inp, q = gen_paged_prefill(ctx, T, Hq, Hkv, D, seed=sum(ctx) + 7 * T, spare_blocks=2)
+    q = (q * q_mul).contiguous()
+    scale = scale_mul / math.sqrt(D)
+    o, lse = afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                    num_splits=splits, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = paged_prefill_oracle(inp, q, True, scale)
+    check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse), l_ref, BF16_LSE_ABS)
+
+
+@pytest.mark.parametrize("T", [8, 20])
+def test_decode_wide_contract_violations_give_nan(afa, T):
+    say(f"case decode wide bad block ids / oversize ctx T{T}")
+    inp, q = gen_paged_prefill([300, 300, 300], T, 64, 8, 128, seed=44, spare_blocks=2, table_pad=0)
+    tbl = inp.block_table.clone()
+    tbl[0, 3] = inp.k_cache.shape[0] + 5          # block id past the pool
+    tbl[1, 17] = -7                                # negative block id (in the second chunk)
+    o, lse = afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, tbl, inp.ctx_lens, num_splits=2)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[0]).all() and torch.isnan(lse[0]).all()
+    assert torch.isnan(o[1]).all() and torch.isnan(lse[1]).all()
+    assert torch.isfinite(o[2]).all() and torch.isfinite(lse[2]).all()
+    ctx2 = inp.ctx_lens.clone()
+    ctx2[2] = inp.block_table.shape[1] * 16 + 1  # more tokens than the table can hold
+    o, lse = afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, inp.block_table, ctx2, num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[2]).all() and torch.isnan(lse[2]).all()
+    assert torch.isfinite(o[0]).all() and torch.isfinite(o[1]).all()
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,D", [(8, 64, 8, 128), (16, 64, 8, 128), (12, 32, 4, 64)])
+def test_decode_wide_single_split_writes_result_directly(afa, T, Hq, Hkv, D):
+    # As for the narrow kernel: one chunk writes bf16 O and lse directly, two
+    # chunks of which the second is empty go through the merge with weights
+    # 1 and 0, and the results are bit-identical, empty sequences included.
+    from attention_flash_fwd_amd import inputs
+    say(f"case decode wide single split T{T} Hq{Hq} Hkv{Hkv} D{D}")
+    ctx = [16, 1, 0, 9, 16, 5, 12]
+    inp = inputs.decode_inputs(ctx, Hq, Hkv, D, seed=23, device="cuda", spare_blocks=2)
+    q = inputs.chunk_queries(len(ctx), T, Hq, D, seed=24, device="cuda")
+    run = lambda s: afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                           num_splits=s)
+    o1, l1 = run(1)
+    o2, l2 = run(2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(torch.isneginf(l1), torch.isneginf(l2))
+    fin = torch.isfinite(l1)
+    assert torch.equal(l1[fin], l2[fin])
+    assert torch.all(o1[2] == 0) and torch.all(torch.isneginf(l1[2]))
+    o_ref, l_ref = paged_prefill_oracle(inp, q, True, 1 / math.sqrt(D))
+    check_o(to_np(o1), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    fin_ref = np.isfinite(l_ref)
+    assert np.array_equal(fin_ref, to_np(fin))
+    check_lse(to_np(l1)[fin_ref], l_ref[fin_ref], BF16_LSE_ABS)
+
+
+@pytest.mark.parametrize("T", [8, 16])
+def test_decode_wide_128k_sampled(afa, T):
+    # The 128K-context cache (4 sequences, 64 query / 8 KV heads) with T new
+    # tokens at the library's split count; sampled (sequence, head, token)
+    # rows of two sequences against the oracle, every token of one head.
+    from attention_flash_fwd_amd import inputs
+    cfg = inputs.DECODE_128K
+    say(f"case {cfg.name} T={T}, library split count (sampled rows)")
+    inp = inputs.decode_config_inputs(cfg, device="cuda")
+    q = inputs.chunk_queries(cfg.batch, T, cfg.n_q_heads, cfg.head_dim, seed=cfg.seed + T, device="cuda")
+    o, lse = afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                    num_splits=0, scale=cfg.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    seqs = [0, cfg.batch - 1]
+    rng = np.random.default_rng(90 + T)
+    rows = [(int(rng.integers(len(seqs))), int(rng.integers(cfg.n_q_heads)), int(rng.integers(T)))
+            for _ in range(24)] + [(1, cfg.n_q_heads - 1, t) for t in range(T)]
+    kv = [inp.logical_kv(b, device="cpu") for b in seqs]
+    k = np.stack([x[0].float().numpy() for x in kv])
+    v = np.stack([x[1].float().numpy() for x in kv])
+    del kv
+    qn = to_np(q)[seqs]
+    o_ref, l_ref = oracle.attention_rows(qn, k, v, True, cfg.scale, rows)
+    got = np.stack([to_np(o[seqs[bi], t, h]) for (bi, h, t) in rows])
+    got_l = np.array([lse[seqs[bi], h, t].item() for (bi, h, t) in rows])
+    check_o(got, o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(got_l, l_ref, BF16_LSE_ABS)
+    del inp, k, v
+    torch.cuda.empty_cache()
