@@ -396,6 +396,14 @@ decode_wide_kernel(DecodeArgs a)
 // Two ring slots: a third (loads two steps ahead) measured no faster.
 constexpr int kRing = 2;
 
+// Dynamic LDS (unused by the kernel) that limits how many workgroups share a
+// CU.  Measured on MI355X: 64-column workgroups at D = 128 run 1.5-3.5%
+// faster two to a CU (54 KiB each) than four (batch 64 with 16 new tokens,
+// 128K context with 8); 128-column workgroups are 35-45% slower alone on a
+// CU than two to a CU (their register use allows two), and keep that.
+template <int D, int NC>
+constexpr unsigned wide_pad() { return (D == 128 && NC == 2) ? 22528u : 0u; }
+
 // Workgroups of one instance resident on a CU at once (queried once).
 template <int D, int NC, bool DYN>
 int wide_resident_per_cu()
@@ -403,7 +411,7 @@ int wide_resident_per_cu()
     static const int n = [] {
         int v = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void *>(&decode_wide_kernel<D, NC, kRing, DYN>),
-                                                         64 * NC, 0) != hipSuccess || v <= 0)
+                                                         64 * NC, wide_pad<D, NC>()) != hipSuccess || v <= 0)
             v = 1;
         return v;
     }();
@@ -417,14 +425,15 @@ hipError_t launch_nc(const DecodeArgs &a, hipStream_t s)
     const long long GT = (long long)(a.Hq / a.Hkv) * a.T;
     const long long n_grp = (GT + kColsPerWave * NC - 1) / (kColsPerWave * NC);
     if (units <= 0 || n_grp <= 0) return hipSuccess;
+    constexpr unsigned pad = wide_pad<D, NC>();
     if (n_grp == 1) {
         // As many workgroups as the GPU holds at once (never more than the
         // items), each taking items until the counter passes the last one.
         const long long grid = std::min<long long>(units, (long long)wide_resident_per_cu<D, NC, true>() * compute_units());
-        hipLaunchKernelGGL((decode_wide_kernel<D, NC, kRing, true>), dim3((unsigned)grid), dim3(64 * NC), 0, s, a);
+        hipLaunchKernelGGL((decode_wide_kernel<D, NC, kRing, true>), dim3((unsigned)grid), dim3(64 * NC), pad, s, a);
     } else {
         const long long grid = (units + 7) / 8 * 8 * n_grp;   // ids padded to whole rounds over the XCDs
-        hipLaunchKernelGGL((decode_wide_kernel<D, NC, kRing, false>), dim3((unsigned)grid), dim3(64 * NC), 0, s, a);
+        hipLaunchKernelGGL((decode_wide_kernel<D, NC, kRing, false>), dim3((unsigned)grid), dim3(64 * NC), pad, s, a);
     }
     return hipGetLastError();
 }

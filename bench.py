@@ -35,9 +35,10 @@ PEAK_HBM_BPS = 8.0e12         # MI355X HBM3E
 COPY_BYTES = 1 << 30          # calibration copy (profiling runs only)
 # Workloads beyond the hot path's step, timed on their own after it (never
 # part of `value` or `ms_per_step`).
-EXTRAS = ("prefill_2k", "chunked_prefill", "decode_multi", "decode_b64_fp8")
+EXTRAS = ("prefill_2k", "chunked_prefill", "decode_multi", "decode_multi_128k", "decode_b64_fp8")
 FP8_SCALE = 1.0 / 32          # per-tensor K and V scale of the fp8 extra
 MULTI_T = 4                   # new tokens per sequence in the multi-token decode extra
+MULTI_128K_T = 16             # new tokens per sequence over the 128K-context cache (128 columns)
 METRIC = "prefill attn TFLOP/s + decode KV GB/s, % of MI355X bf16/HBM peak"
 
 
@@ -380,6 +381,15 @@ def main():
         mo = torch.empty_like(mq)
         mlse = torch.empty((mcfg.batch, mcfg.n_q_heads, multi_t), dtype=torch.float32, device=dev)
         extra_in["decode_multi"] = (mcfg, minp, mq, mws, mo, mlse)
+    if "decode_multi_128k" in parts:
+        kcfg = inputs.DECODE_128K
+        kinp = dec["decode_128k"][1] if "decode_128k" in dec else inputs.decode_config_inputs(kcfg, device=dev)
+        kq = inputs.chunk_queries(kcfg.batch, MULTI_128K_T, kcfg.n_q_heads, kcfg.head_dim, seed=kcfg.seed + 1,
+                                  device=dev)
+        kws = afa.decode_workspace(kq, kinp.k_cache, kinp.block_table, 0)     # the library's split count
+        ko = torch.empty_like(kq)
+        klse = torch.empty((kcfg.batch, kcfg.n_q_heads, MULTI_128K_T), dtype=torch.float32, device=dev)
+        extra_in["decode_multi_128k"] = (kcfg, kinp, kq, kws, ko, klse)
     if "decode_b64_fp8" in parts:
         fcfg = inputs.DECODE_B64
         fctx = inputs.decode_context_lengths(fcfg.batch, fcfg.ctx_min, fcfg.ctx_max, fcfg.seed)
@@ -418,8 +428,8 @@ def main():
         afa.prefill_paged(cq, cinp.k_cache, cinp.v_cache, cinp.block_table, cinp.ctx_lens, causal=True,
                           scale=cp.scale, out=co, lse_out=clse)
 
-    def run_multi():
-        mcfg, minp, mq, mws, mo, mlse = extra_in["decode_multi"]
+    def run_multi(name="decode_multi"):
+        mcfg, minp, mq, mws, mo, mlse = extra_in[name]
         afa.decode_paged_multi(mq, minp.k_cache, minp.v_cache, minp.block_table, minp.ctx_lens,
                                num_splits=0, scale=mcfg.scale, out=mo, lse_out=mlse,
                                workspace=mws)
@@ -443,6 +453,8 @@ def main():
         extra_runners.append(("chunked_prefill", run_chunked))
     if "decode_multi" in extra_in:
         extra_runners.append(("decode_multi", run_multi))
+    if "decode_multi_128k" in extra_in:
+        extra_runners.append(("decode_multi_128k", lambda: run_multi("decode_multi_128k")))
 
     for _ in range(args.warmup):
         for _, fn in runners + extra_runners:
@@ -507,14 +519,15 @@ def main():
             extras[name] = {"workload": fcfg.name.replace("bf16", "fp8kv"), **st, "gbps": gbps,
                             "frac_of_peak": gbps * 1e9 / PEAK_HBM_BPS, "bytes": nb,
                             "num_splits": fcfg.num_splits, "kv_format": "e4m3, per-tensor scale"}
-        elif name == "decode_multi":
+        elif name in ("decode_multi", "decode_multi_128k"):
             mcfg, minp, mq, mws = extra_in[name][:4]
-            nb = decode_bytes(minp, mcfg.n_q_heads) + 2 * (multi_t - 1) * mq[:, 0].numel() * 2
+            tq = mq.shape[1]
+            nb = decode_bytes(minp, mcfg.n_q_heads) + 2 * (tq - 1) * mq[:, 0].numel() * 2
             gbps = nb / (ms * 1e-3) / 1e9
             # the library's split count, read back from its workspace size (fp32 partial
             # outputs and log-sum-exps per (sequence, token, query head, split), 256-byte aligned)
             splits = mws.numel() // (mq.shape[0] * mq.shape[1] * mq.shape[2] * (mq.shape[3] + 1) * 4)
-            extras[name] = {"workload": f"{mcfg.name}_T{multi_t}", **st, "gbps": gbps,
+            extras[name] = {"workload": f"{mcfg.name}_T{tq}", **st, "gbps": gbps,
                             "frac_of_peak": gbps * 1e9 / PEAK_HBM_BPS, "bytes": nb,
                             "num_splits": int(splits)}
     out_parts = {}
