@@ -8,10 +8,12 @@
 // block table).
 //
 // Kernel 1, decode_split: a workgroup of four waves computes one (chunk, KV
-//   head, sequence) item at a time.  With one or two column tiles (below),
-//   as many workgroups as the GPU holds stay resident and take items from a
-//   work counter in the workspace; with more, each workgroup computes one
-//   item.  The G = Hq / Hkv query heads that share the KV head, times
+//   head, sequence) item at a time (or, for one new token over a bf16 cache
+//   with enough work, a (chunk, four KV heads, sequence) item: each wave then
+//   streams one head's blocks of the whole chunk and writes its own
+//   result).  With one or two column tiles (below), as many workgroups as
+//   the GPU holds stay resident and take items from a work counter in the
+//   workspace; with more, each workgroup computes one item.  The G = Hq / Hkv query heads that share the KV head, times
 //   the T new tokens of the sequence (T = 1 for plain decode, several for
 //   speculative verification), are the columns of the matrix-core products,
 //   so each K/V byte is read from HBM once for all of them.  The chunk's
@@ -261,9 +263,10 @@ __device__ __forceinline__ void compute_block(const uint8_t *ks, const uint8_t *
     }
 }
 
-template <int D, int EB, int NCT>
+template <int D, int EB, int NCT, int HPI>
 __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
 {
+    static_assert(HPI == 1 || (HPI == kWaves && NCT == 1), "heads per item: 1, or one per wave with one tile");
     using Gm = Geom<D, EB>;
     // Two ring slots per wave, K and V each in an array of its own so that the
     // compiler's wait for a slot's loads does not also wait for the other's.
@@ -308,7 +311,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     constexpr bool DYN = dynamic_items<NCT>();
     const int n_ct = (GT + 15) / 16;
     const int n_grp = (n_ct + NCT - 1) / NCT;
-    const unsigned n_units = (unsigned)(a.B * a.Hkv * a.splits);
+    const unsigned n_units = (unsigned)(a.B * (a.Hkv / HPI) * a.splits);
     // DYN: thread 0 takes the next item's ticket while the current item's
     // partials merge (hiding the atomic's latency) and passes the item id to
     // the four waves through an LDS word of its own.  One barrier per item
@@ -345,9 +348,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     // registers held across it.
     const int lane = DYN ? opaque((int)(threadIdx.x & 63)) : (int)(threadIdx.x & 63);
     const int l16 = lane & 15, g = lane >> 4;
+    // HPI = kWaves: the item is KV heads HPI j .. HPI j + HPI - 1 of the
+    // chunk, wave w computing head HPI j + w over every block of the chunk,
+    // so that the workgroup reads HPI adjacent head rows of each token at
+    // about the same time.  HPI = 1: one KV head, its blocks dealt to the
+    // waves.
     const int split = unit % a.splits;
-    const int hk = (unit / a.splits) % a.Hkv;
-    const int b = unit / (a.splits * a.Hkv);
+    const int hk = ((unit / a.splits) % (a.Hkv / HPI)) * HPI + (HPI > 1 ? wave : 0);
+    const int b = unit / (a.splits * (a.Hkv / HPI));
     const int col_base = 16 * NCT * grp;            // first column of tile 0; tile c starts 16 c later
 
     // Sequence length through the scalar cache: everything derived from it
@@ -363,8 +371,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     }
     const int blk0 = t_begin / kBS;
     const int nblk = (t_end - t_begin + kBS - 1) / kBS;
-    // This wave's blocks: chunk blocks wave, wave + 4, ...
-    const int nmine = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
+    // This wave's blocks: chunk blocks first, first + kStride, ...
+    constexpr int kStride = HPI > 1 ? 1 : kWaves;
+    const int first = HPI > 1 ? 0 : wave;
+    const int nmine = HPI > 1 ? nblk : (nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0);
 
     // Column col = t G + g holds query head hk G + g of new token t.  Columns
     // past G T (a ragged last tile, or whole tiles of the last group) read
@@ -401,7 +411,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     // here), one block ahead of their use, so that the loop issues no vector
     // loads besides the K/V streams and every wait for a slot is exact.
     const int32_t __attribute__((address_space(4))) *tb =
-        (const int32_t __attribute__((address_space(4))) *)(a.block_table + (size_t)b * a.max_blocks + blk0 + wave);
+        (const int32_t __attribute__((address_space(4))) *)(a.block_table + (size_t)b * a.max_blocks + blk0 + first);
     int phys_next = nmine > 0 ? tb[0] : 0;
 
     // This lane's offset inside a block for each of its DMAs: row
@@ -425,8 +435,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
         int valid = 0;
         if (j < nmine) {
             const int p = phys_next;
-            phys_next = j + 1 < nmine ? tb[kWaves * (j + 1)] : 0;
-            const int tok0 = (blk0 + wave + kWaves * j) * kBS;
+            phys_next = j + 1 < nmine ? tb[kStride * (j + 1)] : 0;
+            const int tok0 = (blk0 + first + kStride * j) * kBS;
             if (p < 0 || p >= a.num_blocks) {
                 bad = true;
             } else {
@@ -437,10 +447,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
         issue_block<Gm>(a.k_cache, a.v_cache, phys, blk_bytes, valid, voff, lane, ks, vs);
     };
     auto valid_rows = [&](int j) __attribute__((always_inline)) {
-        return min(kBS, t_end - (blk0 + wave + kWaves * j) * kBS);
+        return min(kBS, t_end - (blk0 + first + kStride * j) * kBS);
     };
     // Only blocks reaching past ctx - T need the causal check.
-    auto tok0_of = [&](int j) __attribute__((always_inline)) { return (blk0 + wave + kWaves * j) * kBS; };
+    auto tok0_of = [&](int j) __attribute__((always_inline)) { return (blk0 + first + kStride * j) * kBS; };
     auto causal_blk = [&](int j) __attribute__((always_inline)) { return T > 1 && tok0_of(j) + kBS - 1 > ctx - T; };
 
     // Every path through the loop issues the same loads in the same order,
@@ -482,6 +492,35 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (DYN && threadIdx.x == 0) ticket = atomicAdd(a.work_ctr, 1u);
+    if constexpr (HPI > 1) {
+        // Each wave holds its head's whole chunk: normalise and write its
+        // columns straight from the accumulators (lane (g, l16): column l16,
+        // d = 16 db + 4 g .. +3).  Every wave reads the same block ids, so
+        // they agree on `bad`.
+        if (l16 < GT) {
+            const float L = w[0].l;
+            const float inv = bad ? __builtin_nanf("") : (L > 0.f ? a.v_scale / L : 0.f);
+            const float lse = bad ? __builtin_nanf("") : (L > 0.f ? (w[0].m + __log2f(L)) * kLn2 : kNegInf);
+            const int tq = l16 / G, hq = hk * G + l16 % G;
+            const size_t orow = ((size_t)b * T + tq) * a.Hq + hq;
+            if (a.splits == 1) {
+                uint16_t *dst = a.o + orow * D + 4 * g;
+#pragma unroll
+                for (int db = 0; db < D / 16; ++db) {
+                    const f32x4_t x = w[0].o[db] * inv;
+                    *reinterpret_cast<u32x2_t *>(dst + 16 * db) = u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+                }
+                if (g == 0 && a.lse != nullptr) a.lse[((size_t)b * a.Hq + hq) * T + tq] = lse;
+            } else {
+                const size_t row = orow * a.splits + split;
+                float *dst = a.part_o + row * D + 4 * g;
+#pragma unroll
+                for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4_t *>(dst + 16 * db) = w[0].o[db] * inv;
+                if (g == 0) a.part_lse[row] = lse;
+            }
+        }
+        continue;
+    }
     // Wave w's partial O (16 columns x D fp32): bf16 caches put two waves in
     // each of k_s0 / v_s0, fp8 caches one wave in each of the four slots.
     auto merge_area = [&](int v) __attribute__((always_inline)) -> float * {
@@ -670,40 +709,59 @@ __global__ void __launch_bounds__(kThreads) decode_combine_kernel(DecodeArgs a)
 // kernel streams 1-1.5% faster that way (fewer concurrent streams per CU);
 // fp8 caches and several column tiles per workgroup need a second
 // workgroup to hide their heavier per-block work, and keep two or three.
-template <int D, int EB, int NCT>
+template <int D, int EB, int NCT, int HPI>
 constexpr unsigned occupancy_pad() { return (D == 128 && EB == 2 && NCT == 1) ? 32768u : 0u; }
 
 // Split workgroups resident on one CU at once (queried once per kernel).
-template <int D, int EB, int NCT>
+template <int D, int EB, int NCT, int HPI>
 int resident_per_cu()
 {
     static const int n = [] {
         int v = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void *>(&decode_split_kernel<D, EB, NCT>),
-                                                         kThreads, occupancy_pad<D, EB, NCT>()) != hipSuccess || v <= 0)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void *>(&decode_split_kernel<D, EB, NCT, HPI>),
+                                                         kThreads, occupancy_pad<D, EB, NCT, HPI>()) != hipSuccess || v <= 0)
             v = 1;
         return v;
     }();
     return n;
 }
 
-template <int D, int EB, int NCT>
+template <int D, int EB, int NCT, int HPI>
 hipError_t launch_split(const DecodeArgs &a, long long n_ct, hipStream_t s)
 {
-    const long long units = (long long)a.B * a.Hkv * a.splits;
+    const long long units = (long long)a.B * (a.Hkv / HPI) * a.splits;
     const long long n_grp = (n_ct + NCT - 1) / NCT;
     if (units <= 0 || n_ct <= 0) return hipSuccess;
     long long grid;
     if constexpr (dynamic_items<NCT>()) {
         // As many workgroups as the GPU holds at once (never more than the
         // items), each taking items until the counter passes the last one.
-        grid = std::min<long long>(units * n_grp, (long long)resident_per_cu<D, EB, NCT>() * compute_units());
+        grid = std::min<long long>(units * n_grp, (long long)resident_per_cu<D, EB, NCT, HPI>() * compute_units());
     } else {
         grid = (units + 7) / 8 * 8 * n_grp;         // ids padded to whole rounds over the XCDs
     }
-    constexpr unsigned pad = occupancy_pad<D, EB, NCT>();
-    hipLaunchKernelGGL((decode_split_kernel<D, EB, NCT>), dim3((unsigned)grid), dim3(kThreads), pad, s, a);
+    constexpr unsigned pad = occupancy_pad<D, EB, NCT, HPI>();
+    hipLaunchKernelGGL((decode_split_kernel<D, EB, NCT, HPI>), dim3((unsigned)grid), dim3(kThreads), pad, s, a);
     return hipGetLastError();
+}
+
+// Items of kWaves KV heads (one per wave, each wave streaming its head's
+// whole chunk) for single-token decode over a bf16 cache, when there are at
+// least as many such items as compute units and no chunk is longer than 2048
+// tokens.  The workgroup then reads four adjacent head rows of each token at
+// about the same time: a probe streams that pattern at 6.4 TB/s against
+// 5.7-5.9 for one head's rows.  Measured on MI355X against one-head items:
+// batch 64 at 16 chunks 0.839 -> 0.821 ms, batch 4 at 128K with 64 chunks
+// 0.373 -> 0.365 ms, 4 x 8192 tokens at 32 chunks 39 -> 28 us; with fewer
+// items, longer chunks, several new tokens or an fp8 cache (heavier work per
+// block) one-head items were faster (batch 64 at 8 chunks 0.827 against
+// 0.842 ms; fp8 batch 64 at 16 chunks 0.448 against 0.478 ms).
+bool head_group_items(const DecodeArgs &a)
+{
+    if (a.T != 1 || a.Hkv % kWaves != 0) return false;
+    const long long items = (long long)a.B * (a.Hkv / kWaves) * a.splits;
+    const long long max_tokens = (long long)a.max_blocks * kBS;
+    return items >= compute_units() && (max_tokens + a.splits - 1) / a.splits <= 2048;
 }
 
 // Column tiles per workgroup: the fewest groups of at most kMaxTiles tiles,
@@ -717,10 +775,15 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
     const long long nct = n_grp > 0 ? (n_ct + n_grp - 1) / n_grp : 1;
     hipError_t e;
     if (EB == 2 && n_ct > 2) e = launch_decode_wide(a, D, s);   // more than 32 columns, bf16 cache
-    else if (nct <= 1) e = launch_split<D, EB, 1>(a, n_ct, s);
-    else if (nct == 2) e = launch_split<D, EB, 2>(a, n_ct, s);
-    else if (nct == 3) e = launch_split<D, EB, 3>(a, n_ct, s);
-    else e = launch_split<D, EB, kMaxTiles>(a, n_ct, s);
+    else if (nct <= 1) {
+        if constexpr (EB == 2)
+            e = head_group_items(a) ? launch_split<D, EB, 1, kWaves>(a, n_ct, s) : launch_split<D, EB, 1, 1>(a, n_ct, s);
+        else
+            e = launch_split<D, EB, 1, 1>(a, n_ct, s);
+    }
+    else if (nct == 2) e = launch_split<D, EB, 2, 1>(a, n_ct, s);
+    else if (nct == 3) e = launch_split<D, EB, 3, 1>(a, n_ct, s);
+    else e = launch_split<D, EB, kMaxTiles, 1>(a, n_ct, s);
     if (n_ct <= 0 || (long long)a.B * a.Hkv * a.splits <= 0) return e;
     if (e != hipSuccess) return e;
     if (a.splits == 1) return hipSuccess;          // the split kernel wrote the result itself

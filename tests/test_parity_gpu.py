@@ -895,3 +895,57 @@ def test_decode_wide_128k_sampled(afa, T):
     check_lse(got_l, l_ref, BF16_LSE_ABS)
     del inp, k, v
     torch.cuda.empty_cache()
+
+
+# ------------------------------------ single-token decode, four-head items ---
+# With one new token over a bf16 cache, KV heads in multiples of four, at
+# least one item per compute unit and chunks of at most 2048 tokens, the
+# split kernel's items are (chunk, four KV heads, sequence), one head per
+# wave.  Many short sequences reach that regime at small sizes: the cases
+# check every sequence, empty and one-token ones included, at one chunk (the
+# direct write), two and three chunks, and the NaN contract.
+def head_group_regime(B, Hkv, splits, max_tokens):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return Hkv % 4 == 0 and B * (Hkv // 4) * splits >= cus and -(-max_tokens // splits) <= 2048
+
+
+@pytest.mark.parametrize("D,splits", [(128, 1), (128, 2), (128, 3), (64, 2)])
+def test_decode_head_group_items(afa, D, splits):
+    say(f"case decode four-head items D{D} splits{splits}")
+    rng = np.random.default_rng(31 + D + splits)
+    B, Hq, Hkv = 160, 32, 8
+    ctx = [int(x) for x in rng.integers(0, 1500, B)]
+    ctx[:4] = [0, 1, 16, 17]
+    inp = gen_decode(ctx, Hq, Hkv, D, seed=33 + splits)
+    assert head_group_regime(B, Hkv, splits, inp.block_table.shape[1] * 16)
+    o, lse = run_decode(afa, inp, splits)
+    o_ref, l_ref = decode_oracle(inp, 1 / math.sqrt(D))
+    check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(fin, np.isfinite(to_np(lse)))
+    check_lse(to_np(lse)[fin], l_ref[fin], BF16_LSE_ABS)
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
+def test_decode_head_group_items_nan_contract(afa):
+    say("case decode four-head items: bad block ids / oversize ctx")
+    B, Hq, Hkv, D = 160, 32, 8, 128
+    inp = gen_decode([200] * B, Hq, Hkv, D, seed=35, table_pad=0)
+    assert head_group_regime(B, Hkv, 2, inp.block_table.shape[1] * 16)
+    tbl = inp.block_table.clone()
+    tbl[3, 2] = inp.k_cache.shape[0] + 9          # block id past the pool
+    tbl[70, 12] = -1                               # negative block id, second chunk
+    o, lse = afa.decode_paged(inp.q, inp.k_cache, inp.v_cache, tbl, inp.ctx_lens, num_splits=2)
+    torch.cuda.synchronize()
+    bad = torch.zeros(B, dtype=torch.bool)
+    bad[3] = bad[70] = True
+    assert torch.isnan(o[bad]).all() and torch.isnan(lse[bad]).all()
+    assert torch.isfinite(o[~bad]).all() and torch.isfinite(lse[~bad]).all()
+    ctx2 = inp.ctx_lens.clone()
+    ctx2[5] = inp.block_table.shape[1] * 16 + 1   # more tokens than the table can hold
+    o, lse = afa.decode_paged(inp.q, inp.k_cache, inp.v_cache, inp.block_table, ctx2, num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[5]).all() and torch.isnan(lse[5]).all()
+    keep = torch.ones(B, dtype=torch.bool)
+    keep[5] = False
+    assert torch.isfinite(o[keep]).all()
