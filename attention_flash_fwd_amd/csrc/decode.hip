@@ -8,10 +8,9 @@
 // block table).
 //
 // Kernel 1, decode_split: a workgroup of four waves computes one (chunk, KV
-//   head, sequence) item at a time (or, for one new token over a bf16 cache
-//   with enough work, a (chunk, four KV heads, sequence) item: each wave then
-//   streams one head's blocks of the whole chunk and writes its own
-//   result).  With one or two column tiles (below), as many workgroups as
+//   head, sequence) item at a time (or, for one new token with enough work,
+//   a (chunk, four KV heads, sequence) item: each wave then streams one
+//   head's blocks of the whole chunk and writes its own result).  With one or two column tiles (below), as many workgroups as
 //   the GPU holds stay resident and take items from a work counter in the
 //   workspace; with more, each workgroup computes one item.  The G = Hq / Hkv query heads that share the KV head, times
 //   the T new tokens of the sequence (T = 1 for plain decode, several for
@@ -71,6 +70,7 @@ constexpr bool dynamic_items() { return NCT <= 2; }
 template <int D, int NCT>
 constexpr bool qs_in_lds() { return D == 128 && NCT == 4; }
 constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxRanked = 256;     // sequences ranked by length for four-head items
 constexpr uint32_t kOutside = 0x80000000u;   // buffer offset past any block: reads zero
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -320,6 +320,25 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     // which every wave passes after reading it.
     __shared__ unsigned item_slot[1];
     unsigned ticket = 0;                // thread 0: the ticket for the next item
+    // HPI > 1: an item's waves each stream a whole chunk, so a long item
+    // started late would set the kernel's end.  Items are therefore handed
+    // out longest sequence first (list scheduling): each workgroup ranks the
+    // sequences by length (ties by index, a permutation) into an LDS table
+    // as it starts.  More sequences than the table holds keep their order.
+    __shared__ int16_t seq_order[HPI > 1 ? kMaxRanked : 1];
+    const bool ranked = HPI > 1 && DYN && a.B <= kMaxRanked;
+    if (ranked) {
+        for (int i = threadIdx.x; i < a.B; i += kThreads) {
+            const int ci = a.ctx_lens[i];
+            int r = 0;
+            for (int j = 0; j < a.B; ++j) {
+                const int cj = a.ctx_lens[j];
+                r += (cj > ci) | ((cj == ci) & (j < i));
+            }
+            seq_order[r] = (int16_t)i;
+        }
+        __syncthreads();
+    }
     if (DYN && blockIdx.x == 0 && threadIdx.x == 0) atomicExch(a.work_ctr, 0u);
     for (int round = 0;; ++round) {
     int grp, unit;
@@ -355,7 +374,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     // waves.
     const int split = unit % a.splits;
     const int hk = ((unit / a.splits) % (a.Hkv / HPI)) * HPI + (HPI > 1 ? wave : 0);
-    const int b = unit / (a.splits * (a.Hkv / HPI));
+    const int bq = unit / (a.splits * (a.Hkv / HPI));
+    const int b = ranked ? (int)uniform_u32((uint32_t)seq_order[bq]) : bq;
     const int col_base = 16 * NCT * grp;            // first column of tile 0; tile c starts 16 c later
 
     // Sequence length through the scalar cache: everything derived from it
@@ -746,16 +766,17 @@ hipError_t launch_split(const DecodeArgs &a, long long n_ct, hipStream_t s)
 }
 
 // Items of kWaves KV heads (one per wave, each wave streaming its head's
-// whole chunk) for single-token decode over a bf16 cache, when there are at
-// least as many such items as compute units and no chunk is longer than 2048
-// tokens.  The workgroup then reads four adjacent head rows of each token at
-// about the same time: a probe streams that pattern at 6.4 TB/s against
-// 5.7-5.9 for one head's rows.  Measured on MI355X against one-head items:
-// batch 64 at 16 chunks 0.839 -> 0.821 ms, batch 4 at 128K with 64 chunks
+// whole chunk, items handed out longest sequence first) for single-token
+// decode, when there are at least as many such items as compute units and no
+// chunk is longer than 2048 tokens.  The workgroup then reads four adjacent
+// head rows of each token at about the same time: a probe streams that
+// pattern at 6.4 TB/s against 5.7-5.9 for one head's rows.  Measured on
+// MI355X against one-head items: batch 64 at 16 chunks 0.840 -> 0.809 ms
+// (bf16) and 0.448 -> 0.437 ms (e4m3), batch 4 at 128K with 64 chunks
 // 0.373 -> 0.365 ms, 4 x 8192 tokens at 32 chunks 39 -> 28 us; with fewer
-// items, longer chunks, several new tokens or an fp8 cache (heavier work per
-// block) one-head items were faster (batch 64 at 8 chunks 0.827 against
-// 0.842 ms; fp8 batch 64 at 16 chunks 0.448 against 0.478 ms).
+// items, longer chunks or several new tokens one-head items were faster
+// (batch 64 at 8 chunks 0.827 against 0.842 ms; with 4 new tokens 0.845
+// against 0.881-0.964 ms).
 bool head_group_items(const DecodeArgs &a)
 {
     if (a.T != 1 || a.Hkv % kWaves != 0) return false;
@@ -776,10 +797,7 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
     hipError_t e;
     if (EB == 2 && n_ct > 2) e = launch_decode_wide(a, D, s);   // more than 32 columns, bf16 cache
     else if (nct <= 1) {
-        if constexpr (EB == 2)
-            e = head_group_items(a) ? launch_split<D, EB, 1, kWaves>(a, n_ct, s) : launch_split<D, EB, 1, 1>(a, n_ct, s);
-        else
-            e = launch_split<D, EB, 1, 1>(a, n_ct, s);
+        e = head_group_items(a) ? launch_split<D, EB, 1, kWaves>(a, n_ct, s) : launch_split<D, EB, 1, 1>(a, n_ct, s);
     }
     else if (nct == 2) e = launch_split<D, EB, 2, 1>(a, n_ct, s);
     else if (nct == 3) e = launch_split<D, EB, 3, 1>(a, n_ct, s);

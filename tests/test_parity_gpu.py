@@ -949,3 +949,26 @@ def test_decode_head_group_items_nan_contract(afa):
     keep = torch.ones(B, dtype=torch.bool)
     keep[5] = False
     assert torch.isfinite(o[keep]).all()
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_decode_fp8_head_group_items(afa, splits):
+    # The e4m3 cache in the four-head regime, sequences of mixed lengths
+    # (handed out longest first), against the fp8 oracle.
+    from attention_flash_fwd_amd import inputs
+    say(f"case decode_fp8 four-head items splits{splits}")
+    rng = np.random.default_rng(41 + splits)
+    B, Hq, Hkv, D = 160, 32, 8, 128
+    ctx = [int(x) for x in rng.integers(0, 1500, B)]
+    ctx[:3] = [0, 1, 1499]
+    inp = inputs.decode_inputs(ctx, Hq, Hkv, D, seed=43 + splits, device="cuda", spare_blocks=2, table_pad=2,
+                               kv_format="fp8", k_scale=0.04, v_scale=0.07)
+    assert head_group_regime(B, Hkv, splits, inp.block_table.shape[1] * 16)
+    o, lse = afa.decode_paged_fp8(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                  0.04, 0.07, num_splits=splits, scale=1 / math.sqrt(D))
+    torch.cuda.synchronize()
+    o_ref, l_ref = fp8_oracle(inp, inp.q, 1 / math.sqrt(D))
+    check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(fin, np.isfinite(to_np(lse)))
+    check_lse(to_np(lse)[fin], l_ref[fin], BF16_LSE_ABS)
