@@ -207,23 +207,32 @@ decode_wide_kernel(DecodeArgs a)
     auto lookup = [&](int s, int bb) __attribute__((always_inline)) {
         return a.max_blocks > 0 ? tb[min(blk0 + 2 * s + bb, a.max_blocks - 1)] : 0;
     };
-    // Descriptor of block bb of step s (physical id p): rows past the chunk
-    // read zero; an id outside the pool marks the sequence bad and reads
-    // nothing.
-    auto rsrc = [&](const void *cache, int s, int bb, int p) __attribute__((always_inline)) {
-        const int rows = (s < nsteps) ? min(kBS, max(0, t_end - kBS * (blk0 + 2 * s + bb))) : 0;
-        const bool wrong = (rows > 0) & ((p < 0) | (p >= a.num_blocks));
+    // Byte offset and size of block bb of step s (physical id p) for this KV
+    // head: rows past the chunk fall outside the size and read zero; an id
+    // outside the pool marks the sequence bad and reads nothing.  K and V
+    // share them (only the cache base differs).  Branch-free: an unused
+    // block gets id 0 and size 0.
+    const size_t hk_off = (size_t)hk * T::row_bytes;
+    auto span = [&](int s, int bb, int p, size_t &off, uint32_t &num) __attribute__((always_inline)) {
+        int rows = t_end - kBS * (blk0 + 2 * s + bb);
+        rows = rows < 0 ? 0 : (rows > kBS ? kBS : rows);
+        rows = s < nsteps ? rows : 0;
+        const bool wrong = (rows > 0) & ((uint32_t)p >= (uint32_t)a.num_blocks);
         bad = bad | wrong;
         const bool use = (rows > 0) & !wrong;
-        const size_t off = use ? (size_t)(uint32_t)p * blk_bytes + (size_t)hk * T::row_bytes : 0;
-        const uint32_t num = use ? (uint32_t)(rows - 1) * row_stride + T::row_bytes : 0u;
-        return make_rsrc(static_cast<const char *>(cache) + off, num);
+        off = (size_t)(use ? (uint32_t)p : 0u) * blk_bytes + hk_off;
+        num = use ? (uint32_t)(rows - 1) * row_stride + T::row_bytes : 0u;
     };
     int id0 = lookup(0, 0), id1 = lookup(0, 1);
     // Queue step s into (ks, vs); the ids of step s + 1 are read meanwhile.
     auto issue = [&](int s, uint8_t *ks, uint8_t *vs) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t dk0 = rsrc(a.k_cache, s, 0, id0), dk1 = rsrc(a.k_cache, s, 1, id1);
-        const __amdgpu_buffer_rsrc_t dv0 = rsrc(a.v_cache, s, 0, id0), dv1 = rsrc(a.v_cache, s, 1, id1);
+        size_t off0, off1;
+        uint32_t num0, num1;
+        span(s, 0, id0, off0, num0);
+        span(s, 1, id1, off1, num1);
+        const char *kc = static_cast<const char *>(a.k_cache), *vc = static_cast<const char *>(a.v_cache);
+        const __amdgpu_buffer_rsrc_t dk0 = make_rsrc(kc + off0, num0), dk1 = make_rsrc(kc + off1, num1);
+        const __amdgpu_buffer_rsrc_t dv0 = make_rsrc(vc + off0, num0), dv1 = make_rsrc(vc + off1, num1);
 #pragma unroll
         for (int j = 0; j < LPW / 2; ++j)
             buffer_load_lds16(lblk[j] ? dk1 : dk0, ks + 1024 * (wave + NC * j), voff[j]);
@@ -262,16 +271,32 @@ decode_wide_kernel(DecodeArgs a)
     float lsum = 0.f;        // this lane's share of the column's sum
 
     // One step from (ks, vs): scores, softmax, PV.
+    // The schedule is fenced: every K read before the first QK product
+    // (one LDS latency a step instead of one per pair of products), and
+    // every V^T read issued behind the QK products so that the softmax hides
+    // its latency.
     auto compute = [&](int s, const uint8_t *ks, const uint8_t *vs) __attribute__((always_inline)) {
         f32x16_t sc;
+        u32x4_t vf[2][D / 32];
         {
             u32x4_t kf[D / 16];
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) kf[kk] = *reinterpret_cast<const u32x4_t *>(ks + k_rd[kk]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk)
                 sc = mfma_32x32x16_bf16(kf[kk], qf[kk], kk == 0 ? f32x16_t{} : sc);
         }
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const int e = 16 * cc * T::row_bytes;
+                const u32x2_t lo = lds_read_tr16(reinterpret_cast<const uint16_t *>(vs + v_rd[0][db] + e));
+                const u32x2_t hi = lds_read_tr16(reinterpret_cast<const uint16_t *>(vs + v_rd[1][db] + e));
+                vf[cc][db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+            }
+        __builtin_amdgcn_sched_barrier(0);
         // Lane (h, l32) holds tokens 8 (v / 4) + 4 h + v % 4 of the step.
         const int tok0 = kBS * (blk0 + 2 * s);
         if (tok0 + kStep > t_end || (TQ > 1 && tok0 + kStep - 1 > ctx - TQ)) {
@@ -311,19 +336,11 @@ decode_wide_kernel(DecodeArgs a)
         // O^T += V^T P^T over the step's two 16-token halves; the S^T
         // accumulator is the B operand once each product takes its tokens in
         // the accumulator's order.
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-            u32x4_t vf[D / 32];
+        for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const int e = 16 * cc * T::row_bytes;
-                const u32x2_t lo = lds_read_tr16(reinterpret_cast<const uint16_t *>(vs + v_rd[0][db] + e));
-                const u32x2_t hi = lds_read_tr16(reinterpret_cast<const uint16_t *>(vs + v_rd[1][db] + e));
-                vf[db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-            }
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) oacc[db] = mfma_32x32x16_bf16(vf[db], pk[cc], oacc[db]);
-        }
+            for (int db = 0; db < D / 32; ++db) oacc[db] = mfma_32x32x16_bf16(vf[cc][db], pk[cc], oacc[db]);
     };
 
     // Step s: wait for its loads (this wave's, then everyone's via the
