@@ -326,13 +326,18 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     // sequences by length (ties by index, a permutation) into an LDS table
     // as it starts.  More sequences than the table holds keep their order.
     __shared__ int16_t seq_order[HPI > 1 ? kMaxRanked : 1];
+    __shared__ int ctx_s[HPI > 1 ? kMaxRanked : 1];
     const bool ranked = HPI > 1 && DYN && a.B <= kMaxRanked;
     if (ranked) {
+        // Lengths staged in LDS, then compared with broadcast reads.
+        for (int i = threadIdx.x; i < a.B; i += kThreads) ctx_s[i] = a.ctx_lens[i];
+        __syncthreads();
         for (int i = threadIdx.x; i < a.B; i += kThreads) {
-            const int ci = a.ctx_lens[i];
+            const int ci = ctx_s[i];
             int r = 0;
+#pragma unroll 8
             for (int j = 0; j < a.B; ++j) {
-                const int cj = a.ctx_lens[j];
+                const int cj = ctx_s[j];
                 r += (cj > ci) | ((cj == ci) & (j < i));
             }
             seq_order[r] = (int16_t)i;
