@@ -262,3 +262,54 @@ def test_prefill_random_sweep(afa, seed):
         o_ref, l_ref = oracle_paged(inp, q, causal, scale)
     check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
     check_lse(to_np(lse), l_ref, BF16_LSE_ABS)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_random_head_groups(afa, seed):
+    # Single-token decode in the four-KV-head regime (KV heads a multiple of
+    # four, at least one item per compute unit, chunks of at most 2048
+    # tokens), where items are handed out longest sequence first: random
+    # batch (the last seed past the 256 sequences the length ranking holds,
+    # so unranked), heads, group size, head_dim, lengths (some empty), split
+    # counts; odd seeds read an fp8 cache.
+    from attention_flash_fwd_amd import inputs
+    rng = np.random.default_rng(9700 + seed)
+    fp8 = seed % 2 == 1
+    nseq = 300 if seed == 5 else int(rng.integers(64, 257))
+    Hkv = int(rng.choice([4, 8, 12]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    while Hkv * G > 64:
+        G //= 2
+    Hq = Hkv * G
+    D = int(rng.choice([64, 128]))
+    ctx = [0 if rng.random() < 0.05 else int(rng.integers(1, 1500)) for _ in range(nseq)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    splits = int(rng.choice([1, 2, 3, 5]))
+    while nseq * (Hkv // 4) * splits < cus:
+        splits += 1
+    ks, vs = (float(rng.uniform(0.02, 0.06)), float(rng.uniform(0.02, 0.06))) if fp8 else (1.0, 1.0)
+    say(f"case random decode, four-head items, seed{seed}: nseq{nseq} Hq{Hq} Hkv{Hkv} D{D} splits{splits} "
+        f"{'fp8' if fp8 else 'bf16'}")
+    inp = inputs.decode_inputs(ctx, Hq, Hkv, D, seed=1000 + seed, device="cuda", spare_blocks=2,
+                               kv_format="fp8" if fp8 else "bf16", k_scale=ks, v_scale=vs)
+    max_tokens = inp.block_table.shape[1] * 16
+    assert -(-max_tokens // splits) <= 2048
+    scale = 1 / math.sqrt(D)
+    if fp8:
+        o, lse = afa.decode_paged_fp8(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens, ks, vs,
+                                      num_splits=splits, scale=scale)
+    else:
+        o, lse = afa.decode_paged(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                  num_splits=splits, scale=scale)
+    torch.cuda.synchronize()
+    qn = to_np(inp.q)
+    kv = [inp.logical_kv(b, device="cpu") for b in range(nseq)]
+    if fp8:
+        o_ref, l_ref = oracle.decode_fp8(qn, [x[0].numpy() for x in kv], [x[1].numpy() for x in kv], scale, ks, vs)
+    else:
+        o_ref, l_ref = oracle.decode(qn, [x[0].float().numpy() for x in kv], [x[1].float().numpy() for x in kv],
+                                     scale)
+    check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(fin, np.isfinite(to_np(lse)))
+    check_lse(to_np(lse)[fin], l_ref[fin], BF16_LSE_ABS)
