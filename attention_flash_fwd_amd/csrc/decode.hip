@@ -131,14 +131,6 @@ __device__ __forceinline__ void issue_block(const void *kc, const void *vc, long
     }
 }
 
-// Four e4m3 values -> four bf16 (exact: every e4m3 value is a bf16 value).
-__device__ __forceinline__ u32x2_t fp8x4_to_bf16(uint32_t x)
-{
-    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
-    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
-    return u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-}
-
 // Convert this wave's fp8 V block (slot layout Geom<D,1>) to bf16 in the
 // scratch block cv (layout Geom<D,2>): lane L handles row L / 4, a quarter
 // of its elements.
@@ -800,7 +792,7 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
     const long long n_grp = (n_ct + kMaxTiles - 1) / kMaxTiles;
     const long long nct = n_grp > 0 ? (n_ct + n_grp - 1) / n_grp : 1;
     hipError_t e;
-    if (EB == 2 && n_ct > 2) e = launch_decode_wide(a, D, s);   // more than 32 columns, bf16 cache
+    if (decode_wide_supported(D, EB == 1, (long long)(a.Hq / a.Hkv) * a.T)) e = launch_decode_wide(a, D, EB == 1, s);
     else if (nct <= 1) {
         e = head_group_items(a) ? launch_split<D, EB, 1, kWaves>(a, n_ct, s) : launch_split<D, EB, 1, 1>(a, n_ct, s);
     }

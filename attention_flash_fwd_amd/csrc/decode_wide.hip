@@ -1,5 +1,5 @@
-// decode_wide.hip -- split-KV decode over a paged bf16 KV cache for many
-// (token, head) columns: several new tokens per sequence (the verification
+// decode_wide.hip -- split-KV decode over a paged KV cache (bf16, or e4m3
+// at head_dim 128) for many (token, head) columns: several new tokens per sequence (the verification
 // step of speculative decoding, "推理加速" interview notes, section
 // speculative decoding; "GPU Kernel 调度：大模型推理的拐点 2026", paragraph
 // on speculative decoding with Flash-Decoding) or large query-head groups.
@@ -24,6 +24,11 @@
 //   kernel, P rounded to bf16 in the layout of the PV operand
 //   O^T (D x 32 columns) += V^T P^T           D / 16 products
 //
+// e4m3 caches: K operands are widened to bf16 in registers as they are
+// read; after each step's loads land, the waves widen the step's V rows
+// into a shared bf16 copy in LDS (a quarter or half each) and meet at one
+// more barrier, so the transposing V reads are those of the bf16 path.
+//
 // Each wave owns its columns for the whole chunk, so no partials are merged
 // across waves: the normalised output and log-sum-exp of every column go
 // straight to the partial buffers (or, with a single chunk, to the output).
@@ -45,10 +50,10 @@ constexpr int kBS = 16;        // tokens per cache block
 constexpr int kStep = 32;      // tokens per step: two cache blocks
 constexpr int kColsPerWave = 32;
 
-template <int D>
+template <int D, int EB = 2>
 struct WideTile {
-    static constexpr int row_bytes = 2 * D;                  // one token row of one KV head, bf16
-    static constexpr int cpr = D / 8;                        // 16-byte chunks per row
+    static constexpr int row_bytes = EB * D;                 // one token row of one KV head (bf16 or e4m3)
+    static constexpr int cpr = row_bytes / 16;               // 16-byte chunks per row
     static constexpr int rows_per_dma = 1024 / row_bytes;    // rows one wave-wide 16-byte load fills
     static constexpr int dmas = kStep / rows_per_dma;        // such loads per K (or V) slot
     static constexpr int slot_bytes = kStep * row_bytes;
@@ -57,10 +62,10 @@ struct WideTile {
     // Periodic in r with period 16.
     static __device__ __forceinline__ int swz(int r, int c)
     {
-        if constexpr (D == 128)
-            return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
-        else
-            return c ^ ((r >> 1) & 7);
+        if constexpr (EB == 2)
+            return D == 128 ? c ^ (((r & 3) << 2) | ((r >> 2) & 3)) : c ^ ((r >> 1) & 7);
+        else   // rows of 128 or 64 bytes
+            return D == 128 ? c ^ ((r >> 1) & 7) : c ^ ((r >> 2) & 3);
     }
 };
 
@@ -73,6 +78,9 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (lds ? 0 : (0xF << 8)));
 }
 
+// Wait for this wave's LDS accesses only (vector-memory loads stay in flight).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (0x7 << 4)); }
+
 // Workgroup barrier that waits for nothing by itself: the caller's
 // wait_vmcnt decides which loads must have landed.  (A fence-based barrier
 // would wait for every LDS-direct load in flight, including those of the
@@ -80,12 +88,13 @@ __device__ __forceinline__ void wait_vmcnt()
 // LDS accesses across it.
 __device__ __forceinline__ void plain_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int D, int NC, int NS, bool DYN>
+template <int D, int NC, int NS, bool DYN, int EB>
 __global__ void __launch_bounds__(64 * NC) __attribute__((amdgpu_waves_per_eu(2)))
 decode_wide_kernel(DecodeArgs a)
 {
     static_assert(NS == 2 || NS == 3, "ring depth");
-    using T = WideTile<D>;
+    using T = WideTile<D, EB>;      // the cache's rows in the ring
+    using TB = WideTile<D, 2>;      // bf16 rows (V as the transposing reads see it)
     static_assert(T::dmas % NC == 0, "loads split evenly over the waves");
     constexpr int LPW = 2 * T::dmas / NC;          // this wave's loads per step (K and V)
     // One array per slot, so that the compiler's wait before a slot's reads
@@ -94,6 +103,8 @@ decode_wide_kernel(DecodeArgs a)
     __shared__ __attribute__((aligned(1024))) uint8_t v0[T::slot_bytes];
     __shared__ __attribute__((aligned(1024))) uint8_t k1[T::slot_bytes];
     __shared__ __attribute__((aligned(1024))) uint8_t v1[T::slot_bytes];
+    // e4m3 caches: the step's V rows widened to bf16, shared by the waves.
+    __shared__ __attribute__((aligned(1024))) uint8_t cv[EB == 1 ? TB::slot_bytes : 16];
 
     const int lane = threadIdx.x & 63;
     const int wave = (int)uniform_u32(threadIdx.x >> 6);
@@ -244,10 +255,13 @@ decode_wide_kernel(DecodeArgs a)
     };
 
     // ---- LDS read offsets (bytes) ---------------------------------------
-    // K operand of S^T = K Q^T: token row l32, chunk 2 kk + h.
+    // K operand of S^T = K Q^T: token row l32, d = 16 kk + 8 h .. +8 (bf16:
+    // chunk 2 kk + h; e4m3: half h of chunk kk).
     int k_rd[D / 16];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) k_rd[kk] = l32 * T::row_bytes + T::swz(l32, 2 * kk + h) * 16;
+    for (int kk = 0; kk < D / 16; ++kk)
+        k_rd[kk] = EB == 2 ? l32 * T::row_bytes + T::swz(l32, 2 * kk + h) * 16
+                           : l32 * T::row_bytes + T::swz(l32, kk) * 16 + 8 * h;
     // V^T operand via transposing reads: within 16-lane group (hh, dh),
     // source lane s16 points at token row 4 hh + 8 t + s16 / 4 and
     // d = 32 db + 16 dh + 4 (s16 % 4); the second 16 tokens are 16 rows on.
@@ -259,7 +273,7 @@ decode_wide_kernel(DecodeArgs a)
         for (int db = 0; db < D / 32; ++db) {
             const int r = 4 * hh + 8 * t + (s16 >> 2);
             const int d = 32 * db + 16 * dh + 4 * (s16 & 3);
-            v_rd[t][db] = r * T::row_bytes + T::swz(r, d >> 3) * 16 + (d & 7) * 2;
+            v_rd[t][db] = r * TB::row_bytes + TB::swz(r, d >> 3) * 16 + (d & 7) * 2;
         }
 
     f32x16_t oacc[D / 32];
@@ -271,6 +285,27 @@ decode_wide_kernel(DecodeArgs a)
     float lsum = 0.f;        // this lane's share of the column's sum
 
     // One step from (ks, vs): scores, softmax, PV.
+    // e4m3: wave w widens rows [w 32 / NC, (w + 1) 32 / NC) of the V slot,
+    // 16 values (one chunk) per lane and pass, into cv in the bf16 layout.
+    auto widen_v = [&](const uint8_t *vs) __attribute__((always_inline)) {
+        if constexpr (EB == 1) {
+            constexpr int RPW = kStep / NC, PASSES = RPW * T::cpr / 64;
+            static_assert(RPW * T::cpr % 64 == 0, "whole passes");
+#pragma unroll
+            for (int i = 0; i < PASSES; ++i) {
+                const int q = lane + 64 * i;
+                const int r = wave * RPW + q / T::cpr, c = q % T::cpr;
+                const u32x4_t x = *reinterpret_cast<const u32x4_t *>(vs + r * T::row_bytes + T::swz(r, c) * 16);
+                const u32x2_t a0 = fp8x4_to_bf16(x[0]), a1 = fp8x4_to_bf16(x[1]);
+                const u32x2_t a2 = fp8x4_to_bf16(x[2]), a3 = fp8x4_to_bf16(x[3]);
+                *reinterpret_cast<u32x4_t *>(cv + r * TB::row_bytes + TB::swz(r, 2 * c) * 16) =
+                    u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+                *reinterpret_cast<u32x4_t *>(cv + r * TB::row_bytes + TB::swz(r, 2 * c + 1) * 16) =
+                    u32x4_t{a2[0], a2[1], a3[0], a3[1]};
+            }
+        }
+    };
+
     // The schedule is fenced: every K read before the first QK product
     // (one LDS latency a step instead of one per pair of products), and
     // every V^T read issued behind the QK products so that the softmax hides
@@ -281,7 +316,15 @@ decode_wide_kernel(DecodeArgs a)
         {
             u32x4_t kf[D / 16];
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) kf[kk] = *reinterpret_cast<const u32x4_t *>(ks + k_rd[kk]);
+            for (int kk = 0; kk < D / 16; ++kk) {
+                if constexpr (EB == 2) {
+                    kf[kk] = *reinterpret_cast<const u32x4_t *>(ks + k_rd[kk]);
+                } else {
+                    const u32x2_t x = *reinterpret_cast<const u32x2_t *>(ks + k_rd[kk]);
+                    const u32x2_t lo = fp8x4_to_bf16(x[0]), hi = fp8x4_to_bf16(x[1]);
+                    kf[kk] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk)
@@ -291,9 +334,10 @@ decode_wide_kernel(DecodeArgs a)
         for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const int e = 16 * cc * T::row_bytes;
-                const u32x2_t lo = lds_read_tr16(reinterpret_cast<const uint16_t *>(vs + v_rd[0][db] + e));
-                const u32x2_t hi = lds_read_tr16(reinterpret_cast<const uint16_t *>(vs + v_rd[1][db] + e));
+                const int e = 16 * cc * TB::row_bytes;
+                const uint8_t *vb = EB == 2 ? vs : cv;
+                const u32x2_t lo = lds_read_tr16(reinterpret_cast<const uint16_t *>(vb + v_rd[0][db] + e));
+                const u32x2_t hi = lds_read_tr16(reinterpret_cast<const uint16_t *>(vb + v_rd[1][db] + e));
                 vf[cc][db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
             }
         __builtin_amdgcn_sched_barrier(0);
@@ -352,6 +396,14 @@ decode_wide_kernel(DecodeArgs a)
         wait_vmcnt<(NS - 2) * LPW, true>();
         plain_barrier();
         issue(s + NS - 1, kn, vn);
+        if constexpr (EB == 1) {
+            // Widen this wave's share of the step's V rows into cv (free:
+            // every wave passed the barrier after its last reads of it),
+            // then wait for the other waves' shares.
+            widen_v(vs);
+            wait_lgkm0();
+            plain_barrier();
+        }
         compute(s, ks, vs);
     };
     issue(0, k0, v0);
@@ -418,50 +470,61 @@ constexpr int kRing = 2;
 // faster two to a CU (54 KiB each) than four (batch 64 with 16 new tokens,
 // 128K context with 8); 128-column workgroups are 35-45% slower alone on a
 // CU than two to a CU (their register use allows two), and keep that.
-template <int D, int NC>
-constexpr unsigned wide_pad() { return (D == 128 && NC == 2) ? 22528u : 0u; }
+template <int D, int NC, int EB>
+constexpr unsigned wide_pad() { return (D == 128 && NC == 2 && EB == 2) ? 22528u : 0u; }
 
 // Workgroups of one instance resident on a CU at once (queried once).
-template <int D, int NC, bool DYN>
+template <int D, int NC, bool DYN, int EB>
 int wide_resident_per_cu()
 {
     static const int n = [] {
         int v = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void *>(&decode_wide_kernel<D, NC, kRing, DYN>),
-                                                         64 * NC, wide_pad<D, NC>()) != hipSuccess || v <= 0)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void *>(&decode_wide_kernel<D, NC, kRing, DYN, EB>),
+                                                         64 * NC, wide_pad<D, NC, EB>()) != hipSuccess || v <= 0)
             v = 1;
         return v;
     }();
     return n;
 }
 
-template <int D, int NC>
+template <int D, int NC, int EB>
 hipError_t launch_nc(const DecodeArgs &a, hipStream_t s)
 {
     const long long units = (long long)a.B * a.Hkv * a.splits;
     const long long GT = (long long)(a.Hq / a.Hkv) * a.T;
     const long long n_grp = (GT + kColsPerWave * NC - 1) / (kColsPerWave * NC);
     if (units <= 0 || n_grp <= 0) return hipSuccess;
-    constexpr unsigned pad = wide_pad<D, NC>();
+    constexpr unsigned pad = wide_pad<D, NC, EB>();
     if (n_grp == 1) {
         // As many workgroups as the GPU holds at once (never more than the
         // items), each taking items until the counter passes the last one.
-        const long long grid = std::min<long long>(units, (long long)wide_resident_per_cu<D, NC, true>() * compute_units());
-        hipLaunchKernelGGL((decode_wide_kernel<D, NC, kRing, true>), dim3((unsigned)grid), dim3(64 * NC), pad, s, a);
+        const long long grid = std::min<long long>(units, (long long)wide_resident_per_cu<D, NC, true, EB>() * compute_units());
+        hipLaunchKernelGGL((decode_wide_kernel<D, NC, kRing, true, EB>), dim3((unsigned)grid), dim3(64 * NC), pad, s, a);
     } else {
         const long long grid = (units + 7) / 8 * 8 * n_grp;   // ids padded to whole rounds over the XCDs
-        hipLaunchKernelGGL((decode_wide_kernel<D, NC, kRing, false>), dim3((unsigned)grid), dim3(64 * NC), pad, s, a);
+        hipLaunchKernelGGL((decode_wide_kernel<D, NC, kRing, false, EB>), dim3((unsigned)grid), dim3(64 * NC), pad, s, a);
     }
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_wide(const DecodeArgs &a, int head_dim, hipStream_t s)
+// bf16 caches from 33 columns on; e4m3 caches (head_dim 128) from 65: at 64
+// columns the 16-column tiles measured faster there (128K context, 8 new
+// tokens: 0.322 against 0.338 ms), at 128 and 256 the wide kernel (0.617 ->
+// 0.396 ms and 1.115 -> 0.728 ms).
+bool decode_wide_supported(int head_dim, bool kv_fp8, long long columns)
+{
+    if (kv_fp8) return head_dim == 128 && columns > 64;
+    return (head_dim == 128 || head_dim == 64) && columns > 32;
+}
+
+hipError_t launch_decode_wide(const DecodeArgs &a, int head_dim, bool kv_fp8, hipStream_t s)
 {
     const long long GT = (long long)(a.Hq / a.Hkv) * a.T;
-    if (head_dim == 128) return GT <= 64 ? launch_nc<128, 2>(a, s) : launch_nc<128, 4>(a, s);
-    if (head_dim == 64) return GT <= 64 ? launch_nc<64, 2>(a, s) : launch_nc<64, 4>(a, s);
+    if (kv_fp8) return head_dim == 128 && GT > 64 ? launch_nc<128, 4, 1>(a, s) : hipErrorInvalidValue;
+    if (head_dim == 128) return GT <= 64 ? launch_nc<128, 2, 2>(a, s) : launch_nc<128, 4, 2>(a, s);
+    if (head_dim == 64) return GT <= 64 ? launch_nc<64, 2, 2>(a, s) : launch_nc<64, 4, 2>(a, s);
     return hipErrorInvalidValue;
 }
 

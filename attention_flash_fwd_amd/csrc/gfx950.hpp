@@ -61,6 +61,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// Four e4m3 values (one word, value i in byte i) -> four bf16 in two words,
+// with v_cvt_scalef32_pk_bf16_fp8 at scale 1.0 (exact: every e4m3 value is
+// a bf16 value).
+__device__ __forceinline__ u32x2_t fp8x4_to_bf16(uint32_t x)
+{
+    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
+    return u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
 // Combine a value with the one held by the lane 32 positions away
 // (v_permlane32_swap: the two wave halves trade their copies), returning
 // max / sum over the pair in every lane.

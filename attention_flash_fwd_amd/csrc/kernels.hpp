@@ -43,9 +43,11 @@ hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, bool causal, 
 hipError_t launch_prefill_f32(const PrefillArgs &a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_prefill_paged_bf16(const PrefillArgs &a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int head_dim, bool kv_fp8, hipStream_t s);
-// Split kernel for more than 32 (token, head) columns over a bf16 cache
-// (the partials as launch_decode's split kernel writes them; no merge).
-hipError_t launch_decode_wide(const DecodeArgs &a, int head_dim, hipStream_t s);
+// Split kernel for many (token, head) columns (more than 32 over a bf16
+// cache, more than 64 over an e4m3 cache at head_dim 128), writing the
+// partials as launch_decode's split kernel does (no merge).
+bool decode_wide_supported(int head_dim, bool kv_fp8, long long columns);
+hipError_t launch_decode_wide(const DecodeArgs &a, int head_dim, bool kv_fp8, hipStream_t s);
 
 // Device address of the library-held decode workspace of the current device
 // (ATTN_STATIC_SCRATCH_BYTES bytes; looked up once per device), or nullptr if

@@ -972,3 +972,29 @@ def test_decode_fp8_head_group_items(afa, splits):
     fin = np.isfinite(l_ref)
     assert np.array_equal(fin, np.isfinite(to_np(lse)))
     check_lse(to_np(lse)[fin], l_ref[fin], BF16_LSE_ABS)
+
+
+@pytest.mark.parametrize("ctx,T,Hq,Hkv,D,splits", [
+    ([700, 33, 1], 8, 64, 8, 128, 3),          # 64 columns: still the 16-column tiles on e4m3
+    ([700, 95], 16, 64, 8, 128, 2),            # 128 columns: four waves of 32
+    ([250, 81, 0], 20, 64, 8, 128, 4),         # 160 columns: two column groups, an empty sequence
+    ([300, 77], 8, 64, 8, 64, 3),              # D = 64: stays on the 16-column tiles
+])
+def test_decode_fp8_wide_columns(afa, ctx, T, Hq, Hkv, D, splits):
+    # More than 64 (token, head) columns over an e4m3 cache at head_dim 128:
+    # the wide split kernel widens each step's V rows to bf16 in LDS once for
+    # all waves (64 columns and D = 64 stay on the 16-column tiles).
+    from attention_flash_fwd_amd import inputs
+    say(f"case decode_fp8 wide ctx{ctx} T{T} Hq{Hq} Hkv{Hkv} D{D} splits{splits}")
+    inp = inputs.decode_inputs(ctx, Hq, Hkv, D, seed=sum(ctx) + T, device="cuda", spare_blocks=2,
+                               kv_format="fp8", k_scale=0.035, v_scale=0.06)
+    q = inputs.chunk_queries(len(ctx), T, Hq, D, seed=7 + T, device="cuda")
+    scale = 1 / math.sqrt(D)
+    o, lse = afa.decode_paged_fp8(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens, 0.035, 0.06,
+                                  num_splits=splits, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = fp8_oracle(inp, q, scale)
+    check_o(to_np(o), o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(fin, np.isfinite(to_np(lse)))
+    check_lse(to_np(lse)[fin], l_ref[fin], BF16_LSE_ABS)
