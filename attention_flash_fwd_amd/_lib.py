@@ -75,8 +75,7 @@ def load():
         return _lib
     import torch  # noqa: F401  -- maps torch's libamdhip64 first
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                           "or python -m attention_flash_fwd_amd.build")
+        raise RuntimeError(f"{LIB_PATH} is not built; run python -m attention_flash_fwd_amd.build")
     _lib = _declare(ctypes.CDLL(LIB_PATH))
     return _lib
 
