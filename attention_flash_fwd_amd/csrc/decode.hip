@@ -721,13 +721,21 @@ __global__ void __launch_bounds__(kThreads) decode_combine_kernel(DecodeArgs a)
     }
 }
 
-// Dynamic LDS (unused by the kernel) that brings one workgroup to 96 KiB, so
-// that one, not two, fits a CU.  On MI355X the bf16, D = 128, single-tile
-// kernel streams 1-1.5% faster that way (fewer concurrent streams per CU);
-// fp8 caches and several column tiles per workgroup need a second
-// workgroup to hide their heavier per-block work, and keep two or three.
+// Dynamic LDS (unused by the kernel) that sets how many workgroups share a
+// CU.  32 KiB brings the bf16, D = 128, single-tile kernel to 96 KiB, so
+// that one, not two, fits a CU: on MI355X it streams 1-1.5% faster that way
+// (fewer concurrent streams per CU).  8 KiB brings the e4m3, D = 128
+// four-head kernel from about 50 to 58 KiB, two per CU instead of three
+// (batch 64 at 16 chunks 0.436 -> 0.431 ms, other shapes unchanged).
+// One-head fp8 items and several column tiles per workgroup need more
+// workgroups to hide their heavier per-block work and keep their default.
 template <int D, int EB, int NCT, int HPI>
-constexpr unsigned occupancy_pad() { return (D == 128 && EB == 2 && NCT == 1) ? 32768u : 0u; }
+constexpr unsigned occupancy_pad()
+{
+    if (D == 128 && EB == 2 && NCT == 1) return 32768u;
+    if (D == 128 && EB == 1 && NCT == 1 && HPI > 1) return 8192u;
+    return 0u;
+}
 
 // Split workgroups resident on one CU at once (queried once per kernel).
 template <int D, int EB, int NCT, int HPI>
