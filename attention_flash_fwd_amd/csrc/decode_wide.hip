@@ -127,6 +127,7 @@ decode_wide_kernel(DecodeArgs a)
     // written and hands the item to the other waves through an LDS word; the
     // barrier that ends every item orders that write after their reads.
     __shared__ unsigned item_slot[1];
+    __shared__ int bad_s[NC];                       // per wave: a bad block id seen in this item
     unsigned ticket = 0;
     if (DYN && blockIdx.x == 0 && threadIdx.x == 0) atomicExch(a.work_ctr, 0u);
     for (int round = 0;; ++round) {
@@ -195,36 +196,39 @@ decode_wide_kernel(DecodeArgs a)
     }
 
     // ---- K/V stream ----------------------------------------------------
-    // Load j of this wave is load i = wave + NC j of the slot (K: j < LPW / 2,
-    // then V): its 64 lanes fill LDS bytes [1024 i, 1024 i + 1024), rows
-    // rows_per_dma i .. of the step; lane l fills row R = rows_per_dma i +
-    // l / cpr at chunk position l % cpr from cache block R / 16, row R % 16.
+    // A step's loads are four block-loads: the K or the V rows (this KV head)
+    // of the step's cache block bb, that is loads bb kDpb .. bb kDpb + kDpb - 1
+    // of the K or V slot; load i fills LDS bytes [1024 i, 1024 i + 1024),
+    // lane l row rows_per_dma i + l / cpr of the step at chunk position
+    // l % cpr.  Wave w issues block-loads w, w + NC, ...: with four waves one
+    // each (K0, K1, V0, V1), with two the K and V of block w.  Either way a
+    // wave needs the id and descriptor span of one cache block, bb = w % 2.
+    constexpr int kDpb = kBS / T::rows_per_dma;    // loads per block-load
+    static_assert(4 % NC == 0 && 2 * T::dmas == 4 * kDpb, "block-loads split evenly over the waves");
+    const int bb = wave & 1;
     const uint32_t row_stride = (uint32_t)(a.Hkv * T::row_bytes);
     const uint32_t blk_bytes = (uint32_t)kBS * row_stride;
-    uint32_t voff[LPW / 2];
-    int lblk[LPW / 2];                              // cache block (0 or 1) of the step, uniform
+    uint32_t voff[kDpb];
 #pragma unroll
-    for (int j = 0; j < LPW / 2; ++j) {
-        const int i = wave + NC * j;
-        const int R = T::rows_per_dma * i + lane / T::cpr;
-        voff[j] = (uint32_t)(R % kBS) * row_stride + (uint32_t)T::swz(R, lane % T::cpr) * 16u;
-        lblk[j] = (T::rows_per_dma * i) / kBS;
+    for (int k = 0; k < kDpb; ++k) {
+        const int R = T::rows_per_dma * k + lane / T::cpr;     // row of the block (the swizzle has period 16)
+        voff[k] = (uint32_t)R * row_stride + (uint32_t)T::swz(R, lane % T::cpr) * 16u;
     }
     const int32_t __attribute__((address_space(4))) *tb =
         (const int32_t __attribute__((address_space(4))) *)(a.block_table + (size_t)b * a.max_blocks);
-    // Physical ids of step s's two blocks (read through the scalar cache; an
+    // Physical id of block bb of step s (read through the scalar cache; an
     // index clamped into the table row, the value only used for rows that
     // exist).
-    auto lookup = [&](int s, int bb) __attribute__((always_inline)) {
+    auto lookup = [&](int s) __attribute__((always_inline)) {
         return a.max_blocks > 0 ? tb[min(blk0 + 2 * s + bb, a.max_blocks - 1)] : 0;
     };
     // Byte offset and size of block bb of step s (physical id p) for this KV
     // head: rows past the chunk fall outside the size and read zero; an id
-    // outside the pool marks the sequence bad and reads nothing.  K and V
-    // share them (only the cache base differs).  Branch-free: an unused
-    // block gets id 0 and size 0.
+    // outside the pool marks the sequence bad and reads nothing.  Branch-free:
+    // an unused block gets id 0 and size 0.  A sequence is bad for the whole
+    // workgroup: the flags of the two blocks are combined after the stream.
     const size_t hk_off = (size_t)hk * T::row_bytes;
-    auto span = [&](int s, int bb, int p, size_t &off, uint32_t &num) __attribute__((always_inline)) {
+    auto span = [&](int s, int p, size_t &off, uint32_t &num) __attribute__((always_inline)) {
         int rows = t_end - kBS * (blk0 + 2 * s + bb);
         rows = rows < 0 ? 0 : (rows > kBS ? kBS : rows);
         rows = s < nsteps ? rows : 0;
@@ -234,24 +238,23 @@ decode_wide_kernel(DecodeArgs a)
         off = (size_t)(use ? (uint32_t)p : 0u) * blk_bytes + hk_off;
         num = use ? (uint32_t)(rows - 1) * row_stride + T::row_bytes : 0u;
     };
-    int id0 = lookup(0, 0), id1 = lookup(0, 1);
-    // Queue step s into (ks, vs); the ids of step s + 1 are read meanwhile.
+    int id_next = lookup(0);
+    // Queue this wave's block-loads of step s into (ks, vs); the id of step
+    // s + 1 is read meanwhile.
     auto issue = [&](int s, uint8_t *ks, uint8_t *vs) __attribute__((always_inline)) {
-        size_t off0, off1;
-        uint32_t num0, num1;
-        span(s, 0, id0, off0, num0);
-        span(s, 1, id1, off1, num1);
-        const char *kc = static_cast<const char *>(a.k_cache), *vc = static_cast<const char *>(a.v_cache);
-        const __amdgpu_buffer_rsrc_t dk0 = make_rsrc(kc + off0, num0), dk1 = make_rsrc(kc + off1, num1);
-        const __amdgpu_buffer_rsrc_t dv0 = make_rsrc(vc + off0, num0), dv1 = make_rsrc(vc + off1, num1);
+        size_t off;
+        uint32_t num;
+        span(s, id_next, off, num);
 #pragma unroll
-        for (int j = 0; j < LPW / 2; ++j)
-            buffer_load_lds16(lblk[j] ? dk1 : dk0, ks + 1024 * (wave + NC * j), voff[j]);
+        for (int j = 0; j < 4 / NC; ++j) {
+            const bool is_v = ((wave + NC * j) >> 1) != 0;    // uniform
+            const __amdgpu_buffer_rsrc_t r =
+                make_rsrc(static_cast<const char *>(is_v ? a.v_cache : a.k_cache) + off, num);
+            uint8_t *dst = (is_v ? vs : ks) + 1024 * kDpb * bb;
 #pragma unroll
-        for (int j = 0; j < LPW / 2; ++j)
-            buffer_load_lds16(lblk[j] ? dv1 : dv0, vs + 1024 * (wave + NC * j), voff[j]);
-        id0 = lookup(s + 1, 0);
-        id1 = lookup(s + 1, 1);
+            for (int k = 0; k < kDpb; ++k) buffer_load_lds16(r, dst + 1024 * k, voff[k]);
+        }
+        id_next = lookup(s + 1);
     };
 
     // ---- LDS read offsets (bytes) ---------------------------------------
@@ -423,9 +426,16 @@ decode_wide_kernel(DecodeArgs a)
         }
     }
     // The trailing loads (past the chunk: zero fills) land and every wave is
-    // done with the ring before the next item's first loads go there.
+    // done with the ring before the next item's first loads go there.  The
+    // same barrier combines the waves' bad-id flags (each wave checked one of
+    // the two blocks of every step): written before it, read after it, and
+    // written again only after the next item's first barrier, which every
+    // wave reaches after its read.
+    if (lane == 0) bad_s[wave] = bad ? 1 : 0;
     wait_vmcnt<0, true>();
     plain_barrier();
+#pragma unroll
+    for (int w = 0; w < NC; ++w) bad = bad | (bad_s[w] != 0);
     if (DYN && threadIdx.x == 0) ticket = atomicAdd(a.work_ctr, 1u);
 
     // ---- output ------------------------------------------------------------

@@ -821,21 +821,26 @@ def test_decode_wide_scale_and_groups(afa, ctx, T, Hq, Hkv, D, splits, scale_mul
 @pytest.mark.parametrize("T", [8, 20])
 def test_decode_wide_contract_violations_give_nan(afa, T):
     say(f"case decode wide bad block ids / oversize ctx T{T}")
-    inp, q = gen_paged_prefill([300, 300, 300], T, 64, 8, 128, seed=44, spare_blocks=2, table_pad=0)
+    inp, q = gen_paged_prefill([300, 300, 300, 300], T, 64, 8, 128, seed=44, spare_blocks=2, table_pad=0)
     tbl = inp.block_table.clone()
-    tbl[0, 3] = inp.k_cache.shape[0] + 5          # block id past the pool
-    tbl[1, 17] = -7                                # negative block id (in the second chunk)
+    # Each wave fetches one of the two cache blocks of a 32-token step, so
+    # bad ids go in both the second (odd) and the first (even) block of a
+    # step: every column of the sequence must still come out NaN.
+    tbl[0, 3] = inp.k_cache.shape[0] + 5          # block id past the pool (odd block of step 1)
+    tbl[1, 17] = -7                                # negative block id (second chunk, odd block)
+    tbl[3, 4] = inp.k_cache.shape[0]               # first id past the pool (even block of step 2)
     o, lse = afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, tbl, inp.ctx_lens, num_splits=2)
     torch.cuda.synchronize()
-    assert torch.isnan(o[0]).all() and torch.isnan(lse[0]).all()
-    assert torch.isnan(o[1]).all() and torch.isnan(lse[1]).all()
+    for b in (0, 1, 3):
+        assert torch.isnan(o[b]).all() and torch.isnan(lse[b]).all(), b
     assert torch.isfinite(o[2]).all() and torch.isfinite(lse[2]).all()
     ctx2 = inp.ctx_lens.clone()
     ctx2[2] = inp.block_table.shape[1] * 16 + 1  # more tokens than the table can hold
     o, lse = afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, inp.block_table, ctx2, num_splits=1)
     torch.cuda.synchronize()
     assert torch.isnan(o[2]).all() and torch.isnan(lse[2]).all()
-    assert torch.isfinite(o[0]).all() and torch.isfinite(o[1]).all()
+    for b in (0, 1, 3):
+        assert torch.isfinite(o[b]).all(), b
 
 
 @pytest.mark.parametrize("T,Hq,Hkv,D", [(8, 64, 8, 128), (16, 64, 8, 128), (12, 32, 4, 64)])
