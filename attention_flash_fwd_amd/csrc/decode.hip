@@ -197,23 +197,45 @@ __device__ __forceinline__ void compute_block(const uint8_t *ks, const uint8_t *
             }
         }
     }
-    // Lane (g, l16) holds tokens 4 g + v of head l16.  One branch covers the
-    // lazy rescale of every tile, so the accumulators are touched on a
-    // single path.
+    // V^T operand: lane (g, i) receives V[4 g + e][16 db + i], e = 0..3, from
+    // the rows 4 g + l16 / 4 read by its group.  Read now, so that the
+    // softmax below hides the reads' latency.
+    u32x2_t vt[D / 16];
+    {
+        const int vr = 4 * g + (l16 >> 2);
+        const uint8_t *vrow = vs + vr * Gm::row_bytes + ((l16 & 1) << 3);
+        const int vsw = Gm::swz(vr);
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+            const int chunk = 2 * db + ((l16 & 3) >> 1);
+            vt[db] = lds_read_tr16(reinterpret_cast<const uint16_t *>(vrow + ((chunk ^ vsw) << 4)));
+        }
+    }
+    // Lane (g, l16) holds tokens 4 g + v of head l16; the four lanes l16 +
+    // 16 g' hold the column's 16 tokens.  Masking only where the block ends
+    // early or reaches past a causal limit (a uniform branch).  One branch
+    // covers the lazy rescale of every tile, so the accumulators are touched
+    // on a single path.
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) s[c] *= scale_log2;
+    if (valid < kBS || causal) {
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const bool vis = 4 * g + v < valid && (!causal || tok0 + 4 * g + v <= lim[c]);
+                s[c][v] = vis ? s[c][v] : kNegInf;
+            }
+    }
     float m_new[NCT];
     bool grow_any = false;
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const bool vis = 4 * g + v < valid && (!causal || tok0 + 4 * g + v <= lim[c]);
-            const float t = vis ? s[c][v] * scale_log2 : kNegInf;
-            s[c][v] = t;
-            mx = fmaxf(mx, t);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // max over the column's tokens: in-lane, then across the wave's
+        // quarters (v_permlane16_swap, v_permlane32_swap)
+        float mx = fmaxf(fmaxf(s[c][0], s[c][1]), fmaxf(s[c][2], s[c][3]));
+        mx = pair_max_quarters(mx);
+        mx = pair_max_halves(mx);
         m_new[c] = fmaxf(w[c].m, mx);
         grow_any |= m_new[c] > w[c].m + 8.0f;
     }
@@ -240,19 +262,10 @@ __device__ __forceinline__ void compute_block(const uint8_t *ks, const uint8_t *
         }
         pk[c] = u32x2_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
     }
-
-    // V^T operand: lane (g, i) receives V[4 g + e][16 db + i], e = 0..3, from
-    // the rows 4 g + l16 / 4 read by its group.
-    const int vr = 4 * g + (l16 >> 2);
-    const uint8_t *vrow = vs + vr * Gm::row_bytes + ((l16 & 1) << 3);
-    const int vsw = Gm::swz(vr);
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-        const int chunk = 2 * db + ((l16 & 3) >> 1);
-        const u32x2_t vt = lds_read_tr16(reinterpret_cast<const uint16_t *>(vrow + ((chunk ^ vsw) << 4)));
+    for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) w[c].o[db] = mfma_16x16x16_bf16(vt, pk[c], w[c].o[db]);
-    }
+        for (int c = 0; c < NCT; ++c) w[c].o[db] = mfma_16x16x16_bf16(vt[db], pk[c], w[c].o[db]);
 }
 
 template <int D, int EB, int NCT, int HPI>

@@ -80,6 +80,15 @@ __device__ __forceinline__ float pair_max_halves(float x)
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Max with the value held by the lane 16 positions away within each half
+// of the wave (v_permlane16_swap: lanes 16-31 and 0-15, and 48-63 and 32-47,
+// trade their copies), in every lane.
+__device__ __forceinline__ float pair_max_quarters(float x)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float pair_sum_halves(float x)
 {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
