@@ -204,7 +204,7 @@ decode_wide_kernel(DecodeArgs a)
     // each (K0, K1, V0, V1), with two the K and V of block w.  Either way a
     // wave needs the id and descriptor span of one cache block, bb = w % 2.
     constexpr int kDpb = kBS / T::rows_per_dma;    // loads per block-load
-    static_assert(4 % NC == 0 && 2 * T::dmas == 4 * kDpb, "block-loads split evenly over the waves");
+    static_assert((NC == 2 || NC == 4) && 2 * T::dmas == 4 * kDpb, "block-loads split evenly over the waves, one block per wave");
     const int bb = wave & 1;
     const uint32_t row_stride = (uint32_t)(a.Hkv * T::row_bytes);
     const uint32_t blk_bytes = (uint32_t)kBS * row_stride;
