@@ -327,3 +327,17 @@ def test_every_kernel_launch_stub_is_defined():
                          check=True).stdout
     missing = [line for line in out.splitlines() if "__device_stub__" in line]
     assert not missing, missing
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # The benchmark measures one GPU; asking for more exits with a message
+    # before anything touches a device.
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=root)
+    assert r.returncode != 0
+    assert "exactly one GPU" in r.stderr
+    assert r.stdout.strip() == ""
