@@ -73,6 +73,26 @@ int resolve_splits(int batch, int n_kv_heads, int max_blocks, int block_size, in
     // partials and, from two chunks on, the merge kernel) than it gains.
     const long long by_fill = std::min((kFillItems + units - 1) / units, (max_tokens + 255) / 256);
     long long s = std::max(by_length, by_fill);
+    // Two chunks only to fill the second half of the GPU do not pay for the
+    // merge they bring when each sequence fits one 2048-token chunk: one
+    // chunk writes its result directly.  (MI355X, 16 sequences: 1024 tokens
+    // 16.8 us with one chunk against 20.4 us with two, 2048 tokens 26.4
+    // against 28.5 us.)
+    if (s == 2 && by_length <= 1) s = 1;
+    // The decode kernel switches to items of four KV heads (one per wave)
+    // when they give at least one item per compute unit with chunks of at
+    // most 2048 tokens.  When the call already splits and at most doubling
+    // the count reaches that regime (chunks still of 256 tokens or more),
+    // take it.  Measured on MI355X: 16 x 8192 tokens 104.2 -> 98.1 us (4 -> 8
+    // chunks), 4 x 32768 104.1 -> 98.7 us (16 -> 32), 1 x 131072 108.0 ->
+    // 107.0 us (64 -> 128); one-chunk calls stay so (batch 64 at 1024 and
+    // 2048 tokens: 2 chunks were 1-7% slower than one).
+    if (s >= 2 && n_kv_heads % 4 == 0) {
+        const long long groups = (long long)batch * (n_kv_heads / 4);
+        const long long cus = attn::compute_units();
+        const long long s4 = std::max(s, (cus + groups - 1) / groups);
+        if (s4 <= 2 * s && s4 <= (max_tokens + 255) / 256) s = s4;
+    }
     if (s > ATTN_MAX_SPLITS) s = ATTN_MAX_SPLITS;
     if (s < 1) s = 1;
     return (int)s;
