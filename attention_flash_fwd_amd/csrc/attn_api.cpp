@@ -60,6 +60,15 @@ constexpr long long kFillItems = 256;
 // 15.9 us with two), while from 1024 tokens on, batches of 1-4 sequences
 // decode 33-39% faster split.
 constexpr long long kSplitThresholdTokens = 1024;
+// Up to this many tokens, when one chunk per sequence already gives at least
+// a quarter of the items that would fill the GPU twice, two chunks are not
+// worth their merge.  Measured on MI355X, 16 sequences (32 query / 8 KV
+// heads, D 128): one new token, 1024 tokens 16.8 us with one chunk against
+// 20.4 us with two, 2048 tokens 26.4 against 28.5, 4096 tokens 44.7 against
+// 47.2; 2 to 8 new tokens at 1024 tokens 17.0-21.5 against 20.8-26.0 us, at
+// 4096 tokens within -11% to +3%.  With 64 sequences two chunks stay (4096
+// tokens: 185 against 190 us).
+constexpr long long kShortTokens = 4096;
 
 int resolve_splits(int batch, int n_kv_heads, int max_blocks, int block_size, int num_splits)
 {
@@ -73,12 +82,9 @@ int resolve_splits(int batch, int n_kv_heads, int max_blocks, int block_size, in
     // partials and, from two chunks on, the merge kernel) than it gains.
     const long long by_fill = std::min((kFillItems + units - 1) / units, (max_tokens + 255) / 256);
     long long s = std::max(by_length, by_fill);
-    // Two chunks only to fill the second half of the GPU do not pay for the
-    // merge they bring when each sequence fits one 2048-token chunk: one
-    // chunk writes its result directly.  (MI355X, 16 sequences: 1024 tokens
-    // 16.8 us with one chunk against 20.4 us with two, 2048 tokens 26.4
-    // against 28.5 us.)
-    if (s == 2 && by_length <= 1) s = 1;
+    // Two chunks of a short context do not pay for the merge they bring:
+    // one chunk writes its result directly (see kShortTokens).
+    if (s == 2 && max_tokens <= kShortTokens && units < 2 * kFillItems) s = 1;
     // The decode kernel switches to items of four KV heads (one per wave)
     // when they give at least one item per compute unit with chunks of at
     // most 2048 tokens.  When the call already splits and at most doubling
@@ -126,6 +132,7 @@ int resolve_splits_multi(int batch, int seqlen_q, int n_q_heads, int n_kv_heads,
     const long long wgs = units * groups;
     const long long by_fill = std::min((kFillItems + wgs - 1) / wgs, (max_tokens + 255) / 256);
     long long s = std::max(by_length, by_fill);
+    if (s == 2 && max_tokens <= kShortTokens && wgs < 2 * kFillItems) s = 1;
     if (s > ATTN_MAX_SPLITS) s = ATTN_MAX_SPLITS;
     if (s < 1) s = 1;
     return (int)s;

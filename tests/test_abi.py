@@ -226,9 +226,9 @@ def test_workspace_and_split_rules(lib):
     # one chunk per sequence already gives one item per compute unit.
     for (B, Hkv, mb), want in [((64, 8, 2048), 16), ((4, 8, 8192), 64), ((32, 8, 64), 1),
                                ((128, 8, 32), 1), ((8, 8, 256), 4), ((1, 8, 1024), 32),
-                               # half the GPU filled by one 2048-token chunk per sequence:
-                               # one chunk (no merge) rather than two
-                               ((16, 8, 128), 1), ((16, 8, 64), 1), ((16, 8, 256), 2),
+                               # up to 4096 tokens, two chunks only to fill the GPU: one
+                               # chunk (no merge) instead; not with 64 sequences
+                               ((16, 8, 128), 1), ((16, 8, 64), 1), ((16, 8, 256), 1), ((64, 8, 256), 2),
                                # under 1024 tokens: one chunk, however few the sequences
                                ((1, 8, 32), 1), ((16, 8, 63), 1), ((1, 8, 64), 4),
                                # splitting calls whose count at most doubles into the
@@ -267,6 +267,7 @@ def test_multi_token_split_rule(lib):
     assert multi_splits(lib, 8, 4, 32, 8, 128, 256, 0) == 4        # 64 pairs: 256 / 64
     assert multi_splits(lib, 1, 2, 32, 8, 128, 1024, 0) == 32      # 8 pairs: 256 / 8
     assert multi_splits(lib, 1, 2, 8, 8, 64, 4, 0) == 1            # 64 tokens: one chunk of at least 256
+    assert multi_splits(lib, 16, 4, 32, 8, 128, 64, 0) == 1        # 1024 tokens: one chunk, not two for fill
     for B, T, Hq, Hkv, mb in [(1, 3, 4, 1, 1), (2, 16, 16, 1, 300), (8, 5, 64, 8, 9000)]:
         s = multi_splits(lib, B, T, Hq, Hkv, 64, mb, 0)
         assert 1 <= s <= 256
