@@ -105,9 +105,10 @@ int resolve_splits(int batch, int n_kv_heads, int max_blocks, int block_size, in
 }
 
 // Chunks per sequence with seqlen_q new tokens per sequence.  One token:
-// resolve_splits.  Several: every chunk writes a partial output per (token,
-// query head), so with C = (n_q_heads / n_kv_heads) * seqlen_q columns the
-// partial traffic grows with C.  The chunks are then longer, about
+// resolve_splits.  Several, with up to 32 columns C = (n_q_heads /
+// n_kv_heads) * seqlen_q: every chunk writes a partial output per (token,
+// query head), so the partial traffic grows with C.  The chunks are then
+// longer, about
 // 2048 * min(4, max(1, C / 4)) tokens of the longest sequence.  More chunks
 // (none shorter than 256 tokens) are used only until about 256 items, one
 // per compute unit and counted with the column-tile groups, occupy the GPU
@@ -126,12 +127,54 @@ int resolve_splits_multi(int batch, int seqlen_q, int n_q_heads, int n_kv_heads,
     const long long units = (long long)batch * n_kv_heads;
     if (units <= 0 || max_tokens <= 0) return 1;
     const long long cols = (long long)(n_q_heads / n_kv_heads) * seqlen_q;
+    if (cols > 32) {
+        // From 33 columns on the workgroups are wide (64 or 128 columns) and
+        // each token costs them several times the matrix work of the narrow
+        // tiles, so the count follows the workgroups rather than the tokens.
+        // The kernel keeps two workgroups per compute unit resident and hands
+        // out items longest sequence first; the count aims at two items per
+        // compute unit for calls of fewer workgroups than half the compute
+        // units, and at four otherwise (two rounds, which the longest-first
+        // order balances when the lengths differ), with chunks no shorter
+        // than 256 tokens or one token per sixteen partial rows (batch x
+        // query heads x new tokens) the call writes.  Measured on MI355X at
+        // 32 query / 8 KV heads, D 128, 16 and 32 new tokens, 4-64 sequences
+        // of up to 8192 or 32768 tokens: with lengths drawn from 512 up, on
+        // average within 1% of the best explicit count and at most 7% off
+        // (the count that best fits equal lengths was up to 51% off there);
+        // with equal lengths on average within 5% and at most 14% off (64 x
+        // 8192 tokens at 32 new tokens, where one chunk is best).
+        const long long per_wg = cols <= 64 ? 64 : 128;
+        const long long wgs = units * ((cols + per_wg - 1) / per_wg);
+        const long long cus = attn::compute_units();
+        const long long items = (2 * wgs < cus ? 2 : 4) * cus;
+        const long long min_chunk = std::max<long long>(256, units * cols / 16);
+        long long s = std::min(std::max(1LL, items / wgs), std::max(1LL, max_tokens / min_chunk));
+        if (s > ATTN_MAX_SPLITS) s = ATTN_MAX_SPLITS;
+        return (int)s;
+    }
     const long long f = std::min<long long>(4, std::max<long long>(1, cols / 4));
     const long long groups = ((cols + 15) / 16 + 3) / 4;     // workgroups per (chunk, sequence, KV head)
     const long long by_length = (max_tokens + 2048 * f - 1) / (2048 * f);
     const long long wgs = units * groups;
-    const long long by_fill = std::min((kFillItems + wgs - 1) / wgs, (max_tokens + 255) / 256);
+    // Past kShortTokens, calls of at least half as many workgroups as
+    // compute units aim at four items per compute unit, as the wide path
+    // does: with the longest-first item order that balances batches of mixed
+    // lengths.  Measured on MI355X (32 query / 8 KV heads, D 128, 2-8 new
+    // tokens, 16-64 sequences, lengths drawn from 512 up to 16384 or 32768
+    // tokens): one chunk at 32 sequences of up to 16384 tokens took 230 us
+    // with 4 new tokens against 165 us with four chunks; with equal lengths
+    // the count costs up to 18% against the best (32 x 8192 tokens, 8 new
+    // tokens: 231 against 196 us with one chunk).
+    const long long cus = attn::compute_units();
+    long long by_fill;
+    if (max_tokens > kShortTokens && 2 * wgs >= cus)
+        by_fill = std::max(1LL, 4 * cus / wgs);
+    else
+        by_fill = std::min((kFillItems + wgs - 1) / wgs, (max_tokens + 255) / 256);
     long long s = std::max(by_length, by_fill);
+    // Two chunks of a short context do not pay for their merge (as for one
+    // token).
     if (s == 2 && max_tokens <= kShortTokens && wgs < 2 * kFillItems) s = 1;
     if (s > ATTN_MAX_SPLITS) s = ATTN_MAX_SPLITS;
     if (s < 1) s = 1;

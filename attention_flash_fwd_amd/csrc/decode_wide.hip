@@ -49,6 +49,7 @@ namespace {
 constexpr int kBS = 16;        // tokens per cache block
 constexpr int kStep = 32;      // tokens per step: two cache blocks
 constexpr int kColsPerWave = 32;
+constexpr int kMaxRanked = 256;  // sequences ranked by length for the item order
 
 template <int D, int EB = 2>
 struct WideTile {
@@ -129,6 +130,28 @@ decode_wide_kernel(DecodeArgs a)
     __shared__ unsigned item_slot[1];
     __shared__ int bad_s[NC];                       // per wave: a bad block id seen in this item
     unsigned ticket = 0;
+    // DYN: items go out longest sequence first (list scheduling), so that a
+    // long sequence's chunks do not start last: each workgroup ranks the
+    // sequences by length (ties by index, a permutation) into an LDS table
+    // as it starts.  More sequences than the table holds keep their order.
+    __shared__ int16_t seq_order[DYN ? kMaxRanked : 1];
+    __shared__ int ctx_s[DYN ? kMaxRanked : 1];
+    const bool ranked = DYN && a.B <= kMaxRanked;
+    if (ranked) {
+        for (int i = threadIdx.x; i < a.B; i += 64 * NC) ctx_s[i] = a.ctx_lens[i];
+        __syncthreads();
+        for (int i = threadIdx.x; i < a.B; i += 64 * NC) {
+            const int ci = ctx_s[i];
+            int r = 0;
+#pragma unroll 8
+            for (int j = 0; j < a.B; ++j) {
+                const int cj = ctx_s[j];
+                r += (cj > ci) | ((cj == ci) & (j < i));
+            }
+            seq_order[r] = (int16_t)i;
+        }
+        __syncthreads();
+    }
     if (DYN && blockIdx.x == 0 && threadIdx.x == 0) atomicExch(a.work_ctr, 0u);
     for (int round = 0;; ++round) {
     int grp, unit;
@@ -156,7 +179,8 @@ decode_wide_kernel(DecodeArgs a)
     }
     const int split = unit % a.splits;
     const int hk = (unit / a.splits) % a.Hkv;
-    const int b = unit / (a.splits * a.Hkv);
+    const int bq = unit / (a.splits * a.Hkv);
+    const int b = ranked ? (int)uniform_u32((uint32_t)seq_order[bq]) : bq;
 
     const int ctx = ((const int32_t __attribute__((address_space(4))) *)a.ctx_lens)[b];
     bool bad = ctx < 0 || ctx > a.max_blocks * kBS;

@@ -60,6 +60,10 @@ def parse():
                    help="instead of the benchmark, sweep paged decode over context lengths and "
                         "batch sizes with one chunk (Flash-Decoding off), the library's automatic "
                         "count and every explicit count; one JSON line")
+    p.add_argument("--multi-split-sweep", action="store_true",
+                   help="instead of the benchmark, sweep multi-token paged decode (2-32 new tokens "
+                        "per sequence) over equal and mixed context lengths with the library's "
+                        "automatic chunk count and every explicit count; one JSON line")
     p.add_argument("--compare-sdpa", action="store_true",
                    help="instead of the benchmark, time PyTorch's fused attention (SDPA, flash "
                         "backend) beside attn_prefill on the prefill workload; one JSON line")
@@ -218,6 +222,85 @@ def split_sweep(reps):
     }), flush=True)
 
 
+MSWEEP_T = (2, 4, 8, 16, 32)
+MSWEEP_CTX = (8192, 32768)
+MSWEEP_BATCH = (4, 16, 32, 64)
+
+
+def multi_split_sweep(reps):
+    """Chunk counts of attn_decode_paged_multi against every explicit count.
+
+    Workload: bf16 paged decode, 32 query / 8 KV heads, head_dim 128, T new
+    tokens per sequence (4 T columns per KV head: up to 32 in the narrow
+    split kernel, more in the wide one).  Each (T, L, batch) twice: every
+    sequence L tokens long, and lengths drawn uniformly from 512 to L (seeded;
+    the decode workloads' mix).  For each, the automatic count and every
+    power-of-two count up to 64 with chunks of at least 64 tokens; the median
+    of `reps` event-timed calls each, interleaved over three rounds (best
+    round kept)."""
+    import torch
+
+    import attention_flash_fwd_amd as afa
+    from attention_flash_fwd_amd import _lib, inputs
+
+    lib = _lib.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    Hq, Hkv, D = 32, 8, 128
+    rows = []
+    for T in MSWEEP_T:
+        for L in MSWEEP_CTX:
+            for B in MSWEEP_BATCH:
+                for mix in (False, True):
+                    ctx = inputs.decode_context_lengths(B, 512, L, seed=L + B) if mix else [L] * B
+                    inp = inputs.decode_inputs(ctx, Hq, Hkv, D, seed=L + B + T, device=dev)
+                    q = inputs.chunk_queries(B, T, Hq, D, seed=7, device=dev)
+                    o = torch.empty_like(q)
+                    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+                    mb = inp.block_table.shape[1]
+                    per_split = B * T * Hq * (D + 1) * 4
+                    auto = int(lib.attn_decode_multi_workspace_bytes(B, T, Hq, Hkv, D, mb, 16, 0) // per_split)
+                    counts = sorted(set([1] + [c for c in (2, 4, 8, 16, 32, 64) if (L + c - 1) // c >= 64] + [auto]))
+                    wss = {c: torch.empty(int(lib.attn_decode_multi_workspace_bytes(B, T, Hq, Hkv, D, mb, 16, c)),
+                                          dtype=torch.uint8, device=dev) for c in counts}
+
+                    def call(c):
+                        afa.decode_paged_multi(q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                                               num_splits=c, out=o, lse_out=lse, workspace=wss[c])
+
+                    best = {c: float("inf") for c in counts}
+                    for _ in range(3):
+                        for c in counts:
+                            for _ in range(3):
+                                call(c)
+                            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                                   for _ in range(reps)]
+                            for a_ev, b_ev in evs:
+                                a_ev.record(stream)
+                                call(c)
+                                b_ev.record(stream)
+                            torch.cuda.synchronize()
+                            best[c] = min(best[c], stats([a_ev.elapsed_time(b_ev) for a_ev, b_ev in evs])["ms_median"])
+                    c_best = min(best, key=best.get)
+                    row = {"tokens": T, "ctx": L, "batch": B, "lengths": "mixed" if mix else "equal",
+                           "auto_splits": auto, "auto_us": best[auto] * 1e3, "best_splits": c_best,
+                           "best_us": best[c_best] * 1e3, "auto_vs_best": best[auto] / best[c_best],
+                           "by_splits_us": {str(c): best[c] * 1e3 for c in counts}}
+                    rows.append(row)
+                    print(f"multi sweep T {T} ctx {L} batch {B} {row['lengths']}: auto({auto}) {row['auto_us']:.1f} us, "
+                          f"best({c_best}) {row['best_us']:.1f} us", file=sys.stderr, flush=True)
+                    del inp, wss, o, lse, q
+                    torch.cuda.empty_cache()
+    summary = {}
+    for kind in ("equal", "mixed"):
+        r = [x["auto_vs_best"] for x in rows if x["lengths"] == kind]
+        summary[kind] = {"shapes": len(r), "mean_auto_vs_best": sum(r) / len(r), "max_auto_vs_best": max(r),
+                         "within_5pct": sum(1 for x in r if x <= 1.05)}
+    print(json.dumps({"sweep": "multi_token_split_count",
+                      "workload": "paged_decode_multi_h32kv8_d128_bf16, equal and mixed (512..L) contexts",
+                      "reps": reps, "rows": rows, "summary": summary}), flush=True)
+
+
 def decode_bytes(inp, n_q_heads):
     """Algorithmic bytes of one paged decode call: K and V of every cached
     token once per KV head, Q and O once, the used block-table entries and
@@ -330,6 +413,9 @@ def main():
         return
     if args.split_sweep:
         split_sweep(reps=max(5, min(args.steps, 50)))
+        return
+    if args.multi_split_sweep:
+        multi_split_sweep(reps=max(5, min(args.steps, 50)))
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "

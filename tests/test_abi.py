@@ -268,6 +268,23 @@ def test_multi_token_split_rule(lib):
     assert multi_splits(lib, 1, 2, 32, 8, 128, 1024, 0) == 32      # 8 pairs: 256 / 8
     assert multi_splits(lib, 1, 2, 8, 8, 64, 4, 0) == 1            # 64 tokens: one chunk of at least 256
     assert multi_splits(lib, 16, 4, 32, 8, 128, 64, 0) == 1        # 1024 tokens: one chunk, not two for fill
+    # Past 4096 tokens, from half as many workgroups as compute units on:
+    # about four items per compute unit.
+    assert multi_splits(lib, 24, 8, 32, 8, 128, 512, 0) == 5       # 192 workgroups: 1024 // 192
+    assert multi_splits(lib, 16, 8, 32, 8, 128, 1024, 0) == 8      # 128 workgroups: 1024 / 128
+    assert multi_splits(lib, 16, 8, 32, 8, 128, 256, 0) == 1       # 4096 tokens: one chunk, not two
+    # More than 32 columns (wide workgroups of 64 or 128 columns): chunks
+    # until about two items per compute unit (four from 128 workgroups on),
+    # none shorter than 256 tokens or (batch x query heads x tokens) / 16.
+    assert multi_splits(lib, 1, 32, 32, 8, 128, 8192, 0) == 64     # 8 workgroups: 512 / 8
+    assert multi_splits(lib, 1, 16, 32, 8, 128, 256, 0) == 16      # 4096 tokens in chunks of 256
+    assert multi_splits(lib, 4, 32, 32, 8, 128, 256, 0) == 16      # 32 workgroups: 512 / 32
+    assert multi_splits(lib, 16, 32, 32, 8, 128, 256, 0) == 4      # chunks of at least 16 * 32 * 32 / 16 = 1024
+    assert multi_splits(lib, 32, 32, 32, 8, 128, 256, 0) == 2      # chunks of at least 2048
+    assert multi_splits(lib, 16, 16, 32, 8, 128, 1024, 0) == 8     # 128 workgroups: 1024 / 128
+    assert multi_splits(lib, 24, 16, 32, 8, 128, 1024, 0) == 5     # 192 workgroups: 1024 // 192
+    assert multi_splits(lib, 64, 16, 32, 8, 128, 1024, 0) == 2     # 512 workgroups: two rounds
+    assert multi_splits(lib, 64, 64, 32, 8, 128, 1024, 0) == 1     # C = 256: two workgroups per pair
     for B, T, Hq, Hkv, mb in [(1, 3, 4, 1, 1), (2, 16, 16, 1, 300), (8, 5, 64, 8, 9000)]:
         s = multi_splits(lib, B, T, Hq, Hkv, 64, mb, 0)
         assert 1 <= s <= 256

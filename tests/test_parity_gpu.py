@@ -270,6 +270,9 @@ def run_decode(afa, inp, splits, scale=None):
     ([900, 64, 1], 16, 1, 128, 5),           # G = 16
     ([300, 45], 8, 2, 64, 4),                # D = 64
     ([4096, 333], 8, 1, 64, 0),              # automatic split count
+    ([4000, 300, 17], 8, 2, 128, 200),       # merge weights past the first 64 splits, empty chunks
+    ([3000, 70], 8, 2, 64, 130),             # D = 64, 130 splits
+    ([5000, 4100], 8, 2, 128, 256),          # the largest split count
 ])
 def test_decode_small(afa, ctx, Hq, Hkv, D, splits):
     say(f"case decode ctx{ctx} Hq{Hq} Hkv{Hkv} D{D} splits{splits}")
