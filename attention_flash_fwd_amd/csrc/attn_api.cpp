@@ -69,6 +69,10 @@ constexpr long long kSplitThresholdTokens = 1024;
 // 4096 tokens within -11% to +3%.  With 64 sequences two chunks stay (4096
 // tokens: 185 against 190 us).
 constexpr long long kShortTokens = 4096;
+// The same rule for one new token stops at 2048 tokens: with lengths drawn
+// from 512 to 4096 tokens, 16 sequences took 38.1 us with one chunk against
+// 30.5 us with two (equal lengths of 4096: 44.7 against 48.0 us).
+constexpr long long kShortTokensOne = 2048;
 
 int resolve_splits(int batch, int n_kv_heads, int max_blocks, int block_size, int num_splits)
 {
@@ -84,19 +88,23 @@ int resolve_splits(int batch, int n_kv_heads, int max_blocks, int block_size, in
     long long s = std::max(by_length, by_fill);
     // Two chunks of a short context do not pay for the merge they bring:
     // one chunk writes its result directly (see kShortTokens).
-    if (s == 2 && max_tokens <= kShortTokens && units < 2 * kFillItems) s = 1;
+    if (s == 2 && max_tokens <= kShortTokensOne && units < 2 * kFillItems) s = 1;
     // The decode kernel switches to items of four KV heads (one per wave)
     // when they give at least one item per compute unit with chunks of at
     // most 2048 tokens.  When the call already splits and at most doubling
-    // the count reaches that regime (chunks still of 256 tokens or more),
-    // take it.  Measured on MI355X: 16 x 8192 tokens 104.2 -> 98.1 us (4 -> 8
-    // chunks), 4 x 32768 104.1 -> 98.7 us (16 -> 32), 1 x 131072 108.0 ->
-    // 107.0 us (64 -> 128); one-chunk calls stay so (batch 64 at 1024 and
-    // 2048 tokens: 2 chunks were 1-7% slower than one).
+    // the count gives two such items per compute unit (chunks still of 256
+    // tokens or more), take it: with two, the longest-first order balances
+    // batches of mixed lengths, which one item per compute unit cannot
+    // (lengths drawn from 512 up to 4096 tokens, 64 sequences: 4 chunks
+    // 110.7 us, 2 chunks 127.1 us; up to 8192 tokens, 16 sequences: 8 chunks
+    // (one item per compute unit) 50.1 us against 45.2 us with 4).  Equal
+    // lengths lose a little against one item per compute unit (16 x 8192
+    // tokens: 102.9 us at 4 chunks against 97.3 at 8).  One-chunk calls stay
+    // so (batch 64 at 1024 and 2048 tokens: 2 chunks were 1-7% slower).
     if (s >= 2 && n_kv_heads % 4 == 0) {
         const long long groups = (long long)batch * (n_kv_heads / 4);
         const long long cus = attn::compute_units();
-        const long long s4 = std::max(s, (cus + groups - 1) / groups);
+        const long long s4 = std::max(s, (2 * cus + groups - 1) / groups);
         if (s4 <= 2 * s && s4 <= (max_tokens + 255) / 256) s = s4;
     }
     if (s > ATTN_MAX_SPLITS) s = ATTN_MAX_SPLITS;

@@ -144,10 +144,12 @@ def split_sweep(reps):
     enabled and disabled over sequence lengths, find the knee, and check that
     where splitting applies it is at least 30% faster).
 
-    Workload: bf16 paged decode, 32 query / 8 KV heads, head_dim 128, equal
-    context lengths per batch, shuffled 16-token blocks.  For each (context,
-    batch): one chunk (splitting off), the library's automatic count, and
-    every power-of-two count up to 256 (chunks of at least 16 tokens); the
+    Workload: bf16 paged decode, 32 query / 8 KV heads, head_dim 128,
+    shuffled 16-token blocks; each (context L, batch) with equal lengths, and
+    (from 1024 tokens and 4 sequences on) again with lengths drawn uniformly
+    from 512 to L (seeded).  For each: one chunk (splitting off), the
+    library's automatic count, and every power-of-two count up to 256
+    (chunks of at least 16 tokens); the
     median of `reps` event-timed calls each, interleaved over three rounds
     (best round kept).  Batch 64 at 131072 tokens (34 GB of cache) is left
     out; the other shapes fit with room to spare."""
@@ -161,64 +163,71 @@ def split_sweep(reps):
     stream = torch.cuda.current_stream(dev)
     Hq, Hkv, D = 32, 8, 128
     rows = []
-    for L in SWEEP_CTX:
-        for B in SWEEP_BATCH:
-            if L * B > 32768 * 64:
-                continue
-            inp = inputs.decode_inputs([L] * B, Hq, Hkv, D, seed=L + B, device=dev)
-            counts = [1] + [c for c in (2, 4, 8, 16, 32, 64, 128, 256) if (L + c - 1) // c >= 16]
-            auto = afa.decode_num_splits(B, Hkv, inp.block_table.shape[1], 16, 0)
-            o = torch.empty_like(inp.q)
-            lse = torch.empty(inp.q.shape[:2], dtype=torch.float32, device=dev)
-            wss = {c: afa.decode_workspace(inp.q, inp.k_cache, inp.block_table, c)
-                   for c in set(counts + [auto])}
+    shapes = [(L, B, False) for L in SWEEP_CTX for B in SWEEP_BATCH if L * B <= 32768 * 64]
+    shapes += [(L, B, True) for L in SWEEP_CTX for B in SWEEP_BATCH if L * B <= 32768 * 64 and L > 512 and B > 1]
+    for L, B, mix in shapes:
+        ctx = inputs.decode_context_lengths(B, 512, L, seed=L + B) if mix else [L] * B
+        inp = inputs.decode_inputs(ctx, Hq, Hkv, D, seed=L + B, device=dev)
+        counts = [1] + [c for c in (2, 4, 8, 16, 32, 64, 128, 256) if (L + c - 1) // c >= 16]
+        auto = afa.decode_num_splits(B, Hkv, inp.block_table.shape[1], 16, 0)
+        o = torch.empty_like(inp.q)
+        lse = torch.empty(inp.q.shape[:2], dtype=torch.float32, device=dev)
+        wss = {c: afa.decode_workspace(inp.q, inp.k_cache, inp.block_table, c)
+               for c in set(counts + [auto])}
 
-            def call(c):
-                afa.decode_paged(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
-                                 num_splits=c, out=o, lse_out=lse, workspace=wss[c])
+        def call(c):
+            afa.decode_paged(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens,
+                             num_splits=c, out=o, lse_out=lse, workspace=wss[c])
 
-            best = {c: float("inf") for c in wss}
-            for _ in range(3):
-                for c in wss:
-                    for _ in range(3):
-                        call(c)
-                    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                           for _ in range(reps)]
-                    for a_ev, b_ev in evs:
-                        a_ev.record(stream)
-                        call(c)
-                        b_ev.record(stream)
-                    torch.cuda.synchronize()
-                    best[c] = min(best[c], stats([a_ev.elapsed_time(b_ev) for a_ev, b_ev in evs])["ms_median"])
-            c_best = min(best, key=best.get)
-            row = {"ctx": L, "batch": B, "off_us": best[1] * 1e3, "auto_splits": auto,
-                   "auto_us": best[auto] * 1e3, "best_splits": c_best, "best_us": best[c_best] * 1e3,
-                   "auto_vs_best": best[auto] / best[c_best], "auto_speedup_vs_off": best[1] / best[auto],
-                   "by_splits_us": {str(c): best[c] * 1e3 for c in sorted(best)}}
-            rows.append(row)
-            print(f"sweep ctx {L} batch {B}: off {row['off_us']:.1f} us, auto({auto}) {row['auto_us']:.1f} us, "
-                  f"best({c_best}) {row['best_us']:.1f} us", file=sys.stderr, flush=True)
-            del inp, wss, o, lse
-            torch.cuda.empty_cache()
+        best = {c: float("inf") for c in wss}
+        for _ in range(3):
+            for c in wss:
+                for _ in range(3):
+                    call(c)
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(reps)]
+                for a_ev, b_ev in evs:
+                    a_ev.record(stream)
+                    call(c)
+                    b_ev.record(stream)
+                torch.cuda.synchronize()
+                best[c] = min(best[c], stats([a_ev.elapsed_time(b_ev) for a_ev, b_ev in evs])["ms_median"])
+        c_best = min(best, key=best.get)
+        row = {"ctx": L, "batch": B, "lengths": "mixed" if mix else "equal",
+               "off_us": best[1] * 1e3, "auto_splits": auto,
+               "auto_us": best[auto] * 1e3, "best_splits": c_best, "best_us": best[c_best] * 1e3,
+               "auto_vs_best": best[auto] / best[c_best], "auto_speedup_vs_off": best[1] / best[auto],
+               "by_splits_us": {str(c): best[c] * 1e3 for c in sorted(best)}}
+        rows.append(row)
+        print(f"sweep ctx {L} batch {B} {row['lengths']}: off {row['off_us']:.1f} us, auto({auto}) {row['auto_us']:.1f} us, "
+              f"best({c_best}) {row['best_us']:.1f} us", file=sys.stderr, flush=True)
+        del inp, wss, o, lse
+        torch.cuda.empty_cache()
     # The page's threshold policy: split (at the library's count) only when
-    # the context reaches the threshold, else one chunk.
+    # the context reaches the threshold, else one chunk (equal lengths).
+    eq = [r for r in rows if r["lengths"] == "equal"]
+    mixed = [r for r in rows if r["lengths"] == "mixed"]
     policy = {}
     for t in SWEEP_THRESHOLDS:
-        tot = sum((r["auto_us"] if r["ctx"] >= t else r["off_us"]) for r in rows)
+        tot = sum((r["auto_us"] if r["ctx"] >= t else r["off_us"]) for r in eq)
         policy[str(t)] = {"sum_us_over_shapes": tot}
-    tot_auto = sum(r["auto_us"] for r in rows)
+    tot_auto = sum(r["auto_us"] for r in eq)
     # Where splitting applies (the library picks more than one chunk), how
     # much faster than one chunk is it?
-    split_rows = [r for r in rows if r["auto_splits"] > 1]
+    split_rows = [r for r in eq if r["auto_splits"] > 1]
     print(json.dumps({
         "sweep": "flash_decoding_split_threshold",
-        "workload": "paged_decode_h32kv8_d128_bf16, equal contexts per batch",
+        "workload": "paged_decode_h32kv8_d128_bf16, equal contexts per batch, and contexts drawn from 512..L",
         "reps": reps, "rows": rows, "threshold_policy": policy,
         "library_policy_sum_us": tot_auto,
-        "auto_within_5pct_of_best": sum(1 for r in rows if r["auto_vs_best"] <= 1.05),
-        "shapes": len(rows),
+        "auto_within_5pct_of_best": sum(1 for r in eq if r["auto_vs_best"] <= 1.05),
+        "shapes": len(eq),
         "split_shapes_30pct_faster_than_off": sum(1 for r in split_rows if r["auto_speedup_vs_off"] >= 1 / 0.7),
         "split_shapes": len(split_rows),
+        "mixed": {"shapes": len(mixed),
+                  "auto_within_5pct_of_best": sum(1 for r in mixed if r["auto_vs_best"] <= 1.05),
+                  "mean_auto_vs_best": sum(r["auto_vs_best"] for r in mixed) / max(1, len(mixed)),
+                  "max_auto_vs_best": max((r["auto_vs_best"] for r in mixed), default=1.0)},
     }), flush=True)
 
 

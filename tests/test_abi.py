@@ -226,16 +226,17 @@ def test_workspace_and_split_rules(lib):
     # one chunk per sequence already gives one item per compute unit.
     for (B, Hkv, mb), want in [((64, 8, 2048), 16), ((4, 8, 8192), 64), ((32, 8, 64), 1),
                                ((128, 8, 32), 1), ((8, 8, 256), 4), ((1, 8, 1024), 32),
-                               # up to 4096 tokens, two chunks only to fill the GPU: one
-                               # chunk (no merge) instead; not with 64 sequences
-                               ((16, 8, 128), 1), ((16, 8, 64), 1), ((16, 8, 256), 1), ((64, 8, 256), 2),
+                               # up to 2048 tokens, two chunks only to fill the GPU: one
+                               # chunk (no merge) instead; not at 4096 tokens
+                               ((16, 8, 128), 1), ((16, 8, 64), 1), ((16, 8, 256), 2),
                                # under 1024 tokens: one chunk, however few the sequences
                                ((1, 8, 32), 1), ((16, 8, 63), 1), ((1, 8, 64), 4),
-                               # splitting calls whose count at most doubles into the
-                               # four-KV-head regime (an item per CU of 256, chunks <= 2048)
-                               ((16, 8, 512), 8), ((4, 8, 2048), 32), ((1, 8, 8192), 128),
+                               # splitting calls whose count at most doubles into two
+                               # four-KV-head items per CU of 256 (chunks <= 2048)
+                               ((64, 8, 256), 4), ((32, 8, 512), 8),
                                # ... but not by more than doubling, nor from one chunk,
                                # nor with KV heads that are not a multiple of four
+                               ((16, 8, 512), 4), ((4, 8, 2048), 16), ((1, 8, 8192), 64),
                                ((8, 8, 256), 4), ((64, 8, 64), 1), ((16, 6, 512), 4)]:
         assert lib.attn_decode_num_splits(B, Hkv, mb, 16, 0) == want, (B, Hkv, mb)
     assert lib.attn_decode_num_splits(-1, 8, 4, 16, 0) == 0
