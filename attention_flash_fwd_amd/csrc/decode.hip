@@ -655,25 +655,33 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
 }
 
 
-// One wave per (sequence, token, query head) row, kWaves rows per workgroup.
-// Lane l owns d = EPL l .. EPL l + EPL - 1 of the row (EPL = D / 64) and
-// the weights of splits l, l + 64, ... (0 past the last split); max and sum
-// come from wave reductions, and the accumulation reads each split's weight
-// from its lane with v_readlane, so the merge needs no LDS and no barrier.
-// Split rows are loaded BLK at a time (the first BLK before the weights are
-// known); indices past the last split are clamped to it and weighted 0, so
-// every load is unconditional.
-template <int D, int BLK>
+// W waves per (sequence, token, query head) row, kWaves / W rows per
+// workgroup.  Lane l owns d = EPL l .. EPL l + EPL - 1 of the row (EPL =
+// D / 64) and the weights of splits l, l + 64, ... (0 past the last split);
+// max and sum come from wave reductions (every wave of a row forms them),
+// and the accumulation reads each split's weight from its lane with
+// v_readlane.  Wave p of a row takes splits p, p + W, p + 2 W, ..., BLK at a
+// time (the first BLK before the weights are known); indices past the last
+// split are clamped to it and weighted 0, so every load is unconditional.
+// With W = 1 the merge needs no LDS and no barrier; with W > 1 (few rows,
+// many splits) the row's waves add their sums through LDS.
+template <int D, int BLK, int W>
 __global__ void __launch_bounds__(kThreads) decode_combine_kernel(DecodeArgs a)
 {
     static_assert(D == 64 || D == 128, "one or two output elements per lane");
     static_assert(ATTN_MAX_SPLITS <= 256, "four split log-sum-exps per lane");
+    static_assert(kWaves % W == 0 && 64 % (W * BLK) == 0, "a block's splits share one weight register");
     constexpr int EPL = D / 64;
     using vec = typename std::conditional<EPL == 2, f32x2_t, float>::type;
     constexpr int STRIDE = D / EPL;                                   // one split row, in vec units
 
-    const int row = (int)uniform_u32(blockIdx.x * kWaves + (threadIdx.x >> 6));   // (b * T + t) * Hq + hq
-    if (row >= a.B * a.T * a.Hq) return;                                         // whole waves
+    const int wave = (int)uniform_u32(threadIdx.x >> 6);
+    const int rows = a.B * a.T * a.Hq;
+    const int row_raw = blockIdx.x * (kWaves / W) + wave / W;       // (b * T + t) * Hq + hq
+    if (W == 1 && row_raw >= rows) return;                           // whole waves, no barrier below
+    const bool live = row_raw < rows;
+    const int row = min(row_raw, rows - 1);
+    const int part = wave % W;
     const int lane = threadIdx.x & 63;
     const int S = a.splits;
     const float *plse = a.part_lse + (size_t)row * S;
@@ -681,7 +689,7 @@ __global__ void __launch_bounds__(kThreads) decode_combine_kernel(DecodeArgs a)
 
     vec v[BLK];
 #pragma unroll
-    for (int u = 0; u < BLK; ++u) v[u] = po[(size_t)min(u, S - 1) * STRIDE];
+    for (int u = 0; u < BLK; ++u) v[u] = po[(size_t)min(part + W * u, S - 1) * STRIDE];
 
     float M = kNegInf;
     bool nan = false;
@@ -706,20 +714,27 @@ __global__ void __launch_bounds__(kThreads) decode_combine_kernel(DecodeArgs a)
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
 
-    // BLK divides 64, so a block's splits share one weight register.
-    static_assert(64 % BLK == 0, "blocks within one weight register");
     vec acc{};
-    for (int s0 = 0;;) {
-        const int j = s0 >> 6;
+    for (int base = 0;;) {
+        const int j = base >> 6;
         const float wj = j == 0 ? w[0] : j == 1 ? w[1] : j == 2 ? w[2] : w[3];
 #pragma unroll
         for (int u = 0; u < BLK; ++u)
-            acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), (s0 & 63) + u)) * v[u];
-        s0 += BLK;
-        if (s0 >= S) break;
+            acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), (base & 63) + part + W * u)) * v[u];
+        base += W * BLK;
+        if (base >= S) break;
 #pragma unroll
-        for (int u = 0; u < BLK; ++u) v[u] = po[(size_t)min(s0 + u, S - 1) * STRIDE];
+        for (int u = 0; u < BLK; ++u) v[u] = po[(size_t)min(base + part + W * u, S - 1) * STRIDE];
     }
+    if constexpr (W > 1) {
+        __shared__ vec red[kWaves][64];
+        red[wave][lane] = acc;
+        __syncthreads();
+        if (part != 0) return;
+#pragma unroll
+        for (int p = 1; p < W; ++p) acc += red[wave + p][lane];
+    }
+    if (!live) return;
 
     const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
     if constexpr (EPL == 2) {
@@ -737,14 +752,30 @@ __global__ void __launch_bounds__(kThreads) decode_combine_kernel(DecodeArgs a)
     }
 }
 
+// Waves per row: enough waves in flight for the latency of the split loads
+// (about sixteen per compute unit), never more than one per eight splits.
+// Splits per wave load: all of a wave's splits at once up to 16.
 template <int D>
 void launch_combine(const DecodeArgs &a, hipStream_t s)
 {
     const long long rows = (long long)a.B * a.T * a.Hq;
-    const dim3 grid((unsigned)((rows + kWaves - 1) / kWaves)), block(kThreads);
-    if (a.splits <= 2) hipLaunchKernelGGL((decode_combine_kernel<D, 2>), grid, block, 0, s, a);
-    else if (a.splits <= 4) hipLaunchKernelGGL((decode_combine_kernel<D, 4>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_combine_kernel<D, 8>), grid, block, 0, s, a);
+    const long long target = 16LL * compute_units();
+    int W = rows >= target ? 1 : (2 * rows >= target ? 2 : 4);
+    while (W > 1 && a.splits < 8 * W) W >>= 1;
+    const int per_wave = (a.splits + W - 1) / W;
+    const dim3 grid((unsigned)((rows * W + kWaves - 1) / kWaves)), block(kThreads);
+    if (W == 4) {
+        if (per_wave <= 8) hipLaunchKernelGGL((decode_combine_kernel<D, 8, 4>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((decode_combine_kernel<D, 16, 4>), grid, block, 0, s, a);
+    } else if (W == 2) {
+        if (per_wave <= 8) hipLaunchKernelGGL((decode_combine_kernel<D, 8, 2>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((decode_combine_kernel<D, 16, 2>), grid, block, 0, s, a);
+    } else {
+        if (per_wave <= 2) hipLaunchKernelGGL((decode_combine_kernel<D, 2, 1>), grid, block, 0, s, a);
+        else if (per_wave <= 4) hipLaunchKernelGGL((decode_combine_kernel<D, 4, 1>), grid, block, 0, s, a);
+        else if (per_wave <= 8) hipLaunchKernelGGL((decode_combine_kernel<D, 8, 1>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((decode_combine_kernel<D, 16, 1>), grid, block, 0, s, a);
+    }
 }
 
 // Dynamic LDS (unused by the kernel) that sets how many workgroups share a
