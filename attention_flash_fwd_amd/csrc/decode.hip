@@ -752,13 +752,75 @@ __global__ void __launch_bounds__(kThreads) decode_combine_kernel(DecodeArgs a)
     }
 }
 
-// Waves per row: enough waves in flight for the latency of the split loads
-// (about sixteen per compute unit), never more than one per eight splits.
-// Splits per wave load: all of a wave's splits at once up to 16.
+// Up to eight splits: D / 4 lanes per row (4 consecutive d each, so two
+// rows per wave at D = 128), every lane loading its row's few log-sum-exps
+// itself (the lanes of a row read the same addresses) and forming max,
+// weights and sum with no cross-lane step.  All loads are issued at once,
+// indices past the last split clamped to it and weighted 0.
+template <int D, int SMAX>
+__global__ void __launch_bounds__(kThreads) decode_combine_small_kernel(DecodeArgs a)
+{
+    static_assert(D == 64 || D == 128, "16 or 32 lanes per row");
+    constexpr int LPR = D / 4;
+    const int rows = a.B * a.T * a.Hq;
+    const int row = (int)((blockIdx.x * (unsigned)kThreads + threadIdx.x) / LPR);   // (b * T + t) * Hq + hq
+    if (row >= rows) return;                                         // no cross-lane steps below
+    const int c = threadIdx.x % LPR;
+    const int S = a.splits;
+    const float *plse = a.part_lse + (size_t)row * S;
+    const f32x4_t *po = reinterpret_cast<const f32x4_t *>(a.part_o + (size_t)row * S * D) + c;
+
+    f32x4_t v[SMAX];
+    float x[SMAX];
+#pragma unroll
+    for (int u = 0; u < SMAX; ++u) {
+        const int sp = min(u, S - 1);
+        v[u] = po[(size_t)sp * LPR];
+        x[u] = plse[sp];
+    }
+    float M = kNegInf;
+    bool nan = false;
+#pragma unroll
+    for (int u = 0; u < SMAX; ++u)
+        if (u < S) {
+            nan |= (x[u] != x[u]);
+            M = fmaxf(M, x[u]);
+        }
+    float wsum = 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < SMAX; ++u) {
+        const float wv = (u < S && M != kNegInf && x[u] != kNegInf) ? exp2_fast((x[u] - M) * kLog2e) : 0.f;
+        wsum += wv;
+        acc += wv * v[u];
+    }
+    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+    f32x4_t o = acc * inv;
+    if (nan) o = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    const u32x2_t packed = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    *reinterpret_cast<u32x2_t *>(a.o + (size_t)row * D + 4 * c) = packed;
+    if (a.lse != nullptr && c == 0) {
+        const int th = row % (a.T * a.Hq);     // lse is [B, Hq, T]
+        const size_t li = ((size_t)(row / (a.T * a.Hq)) * a.Hq + th % a.Hq) * a.T + th / a.Hq;
+        a.lse[li] = nan ? __builtin_nanf("") : (wsum > 0.f ? M + logf(wsum) : kNegInf);
+    }
+}
+
+// Up to eight splits: the kernel above.  More: W waves per row, enough
+// waves in flight for the latency of the split loads (about sixteen per
+// compute unit), never more than one per eight splits, each loading all of
+// its splits at once up to 16.
 template <int D>
 void launch_combine(const DecodeArgs &a, hipStream_t s)
 {
     const long long rows = (long long)a.B * a.T * a.Hq;
+    if (a.splits <= 8) {
+        const dim3 grid((unsigned)((rows * (D / 4) + kThreads - 1) / kThreads)), block(kThreads);
+        if (a.splits <= 2) hipLaunchKernelGGL((decode_combine_small_kernel<D, 2>), grid, block, 0, s, a);
+        else if (a.splits <= 4) hipLaunchKernelGGL((decode_combine_small_kernel<D, 4>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((decode_combine_small_kernel<D, 8>), grid, block, 0, s, a);
+        return;
+    }
     const long long target = 16LL * compute_units();
     int W = rows >= target ? 1 : (2 * rows >= target ? 2 : 4);
     while (W > 1 && a.splits < 8 * W) W >>= 1;
@@ -771,10 +833,7 @@ void launch_combine(const DecodeArgs &a, hipStream_t s)
         if (per_wave <= 8) hipLaunchKernelGGL((decode_combine_kernel<D, 8, 2>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((decode_combine_kernel<D, 16, 2>), grid, block, 0, s, a);
     } else {
-        if (per_wave <= 2) hipLaunchKernelGGL((decode_combine_kernel<D, 2, 1>), grid, block, 0, s, a);
-        else if (per_wave <= 4) hipLaunchKernelGGL((decode_combine_kernel<D, 4, 1>), grid, block, 0, s, a);
-        else if (per_wave <= 8) hipLaunchKernelGGL((decode_combine_kernel<D, 8, 1>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((decode_combine_kernel<D, 16, 1>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((decode_combine_kernel<D, 16, 1>), grid, block, 0, s, a);
     }
 }
 
