@@ -163,7 +163,10 @@ attn_status_t attn_prefill_paged(const void *q, const void *k_cache, const void 
  * slower), else chunks of about 2048 tokens of the longest sequence the
  * table can hold, or more chunks (none shorter than 256 tokens) when that is
  * needed for about 256 (chunk, sequence, KV head) items, one per compute
- * unit, to occupy the GPU.  Returns 0 for invalid arguments.
+ * unit, to occupy the GPU.  Two chunks of a table of at most 2048 tokens
+ * become one (no merge); a count that at most doubles into two items of
+ * four KV heads per compute unit is doubled.  Returns 0 for invalid
+ * arguments.
  */
 int attn_decode_num_splits(int batch, int n_kv_heads, int max_blocks_per_seq,
                            int block_size, int num_splits);
@@ -291,12 +294,17 @@ attn_status_t attn_decode_paged_noalloc(const void *q, const void *k_cache, cons
  *
  * num_splits <= 0 with seqlen_q > 1: the library's choice, again from the
  * arguments alone.  Each chunk writes a partial output per (token, query
- * head), so with C = (n_q_heads / n_kv_heads) * seqlen_q the chunks are
- * about 2048 * min(4, max(1, C / 4)) tokens of the longest sequence the
- * table can hold.  More chunks (none shorter than 256 tokens) are used only
- * until about 256 items (chunk, sequence, KV head, group of up to 64
- * columns) occupy the GPU.  attn_decode_multi_workspace_bytes
- * sizes the workspace for the same choice.
+ * head); with C = (n_q_heads / n_kv_heads) * seqlen_q:
+ *   C <= 32: chunks of about 2048 * min(4, max(1, C / 4)) tokens of the
+ *     longest sequence the table can hold, and more chunks (none shorter
+ *     than 256 tokens) until about 256 items (chunk, sequence, KV head,
+ *     group of up to 64 columns) occupy the GPU; for tables of more than
+ *     4096 tokens and at least half as many workgroups as compute units,
+ *     about four items per compute unit instead;
+ *   C > 32: about two items per compute unit (four from half as many
+ *     workgroups as compute units on), with chunks of at least 256 tokens
+ *     and at least batch * n_q_heads * seqlen_q / 16 tokens.
+ * attn_decode_multi_workspace_bytes sizes the workspace for the same choice.
  */
 attn_status_t attn_decode_paged_multi(const void *q, const void *k_cache, const void *v_cache,
                                       const int32_t *block_table, const int32_t *ctx_lens,
