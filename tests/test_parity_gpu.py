@@ -270,6 +270,10 @@ def run_decode(afa, inp, splits, scale=None):
     ([900, 64, 1], 16, 1, 128, 5),           # G = 16
     ([300, 45], 8, 2, 64, 4),                # D = 64
     ([4096, 333], 8, 1, 64, 0),              # automatic split count
+    ([2000, 900, 33], 8, 2, 128, 9),         # merge: one wave per row, a clamped block of 16
+    ([2000, 700], 8, 2, 128, 24),            # two waves per row
+    ([3000, 1200, 5], 8, 2, 128, 40),        # four waves per row, a clamped block
+    ([2500, 64], 16, 4, 64, 12),             # D = 64, one wave per row
     ([4000, 300, 17], 8, 2, 128, 200),       # merge weights past the first 64 splits, empty chunks
     ([3000, 70], 8, 2, 64, 130),             # D = 64, 130 splits
     ([5000, 4100], 8, 2, 128, 256),          # the largest split count
