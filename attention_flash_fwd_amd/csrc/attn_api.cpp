@@ -115,17 +115,16 @@ int resolve_splits(int batch, int n_kv_heads, int max_blocks, int block_size, in
 // Chunks per sequence with seqlen_q new tokens per sequence.  One token:
 // resolve_splits.  Several, with up to 32 columns C = (n_q_heads /
 // n_kv_heads) * seqlen_q: every chunk writes a partial output per (token,
-// query head), so the partial traffic grows with C.  The chunks are then
-// longer, about
-// 2048 * min(4, max(1, C / 4)) tokens of the longest sequence.  More chunks
-// (none shorter than 256 tokens) are used only until about 256 items, one
-// per compute unit and counted with the column-tile groups, occupy the GPU
-// (as for one token; short contexts at 2-8 tokens measured best there, e.g.
-// 32 sequences of 1024 tokens at one chunk, 25 us against 35 us at the two
-// a 512 target gave).  (Measured on
-// MI355X against the single-token rule: batch 64 with contexts up to 32K,
-// 2-8 tokens: 3-5% faster; batch 4 at 128K, 8 tokens: 14% faster, 2-4
-// tokens within 1%.)
+// query head), so the partial traffic grows with C, and the chunks are
+// longer, about 2048 * min(4, max(1, C / 4)) tokens of the longest
+// sequence.  More chunks (none shorter than 256 tokens) are added until
+// about 256 items, one per compute unit and counted with the column-tile
+// groups, occupy the GPU (as for one token; short contexts at 2-8 tokens
+// measured best there, e.g. 32 sequences of 1024 tokens at one chunk, 25 us
+// against 35 us at the two a 512 target gave), or, for longer tables and
+// larger calls, about four items per compute unit (below).  Against the
+// single-token rule (MI355X): batch 64 with contexts up to 32K, 2-8 tokens,
+// 3-5% faster; batch 4 at 128K, 8 tokens, 14% faster, 2-4 tokens within 1%.
 int resolve_splits_multi(int batch, int seqlen_q, int n_q_heads, int n_kv_heads, int max_blocks,
                          int block_size, int num_splits)
 {
