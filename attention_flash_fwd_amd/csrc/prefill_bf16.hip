@@ -29,12 +29,16 @@
 //                   ds_read_b64_tr_b16).  The LDS reads run ahead of the
 //                   products, and this part runs at raised wave priority.
 //     softmax part  of tile s: mask (only tiles crossing the diagonal or the
-//                   end of the keys), row max (in-lane plus one exchange of the
-//                   wave halves), lazy rescale (the exponent reference m only
-//                   moves when the row max has grown by more than 2^8),
-//                   P = 2^(s c - m): one FMA + one v_exp_f32 per score, rounded
-//                   to bf16 (RNE) in the layout of the PV operand; the row sum
-//                   adds the fp32 P, so lse keeps fp32 accuracy
+//                   end of the keys), P = 2^(s c - m): one FMA + one v_exp_f32
+//                   per score, rounded to bf16 (RNE) in the layout of the PV
+//                   operand; the row sum adds the fp32 P, so lse keeps fp32
+//                   accuracy.  The exponent reference m is rescaled lazily: it
+//                   only has to keep every P at most 2^8, and as long as each
+//                   lane's tile sum stays within 2^8 the tile needs no row max
+//                   at all.  Only a row's first tile, or a tile whose scores
+//                   grew past that bound, takes the row max (in-lane plus one
+//                   exchange of the wave halves), rescales O and l, and forms
+//                   P again.
 //     group 0 runs [matrix(s), softmax(s)], group 1 [softmax(s-1), matrix(s)];
 //     every wave issues its share of the loads of K(s+1) and V(s), which land
 //     by the step's closing barrier.
@@ -427,39 +431,59 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int n_items)
                     sc[kb][v] = ko <= lim ? sc[kb][v] : kNegInf;
                 }
         }
-        // Row max of the raw scores (c > 0, so scaling preserves order), as
-        // four independent partial maxima.
-        float mp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+        // P = 2^(s c - m) -> bf16 pairs; returns this lane's sum of the fp32
+        // values (the row sum keeps fp32 accuracy).
+        auto exp_tile = [&](float nm) __attribute__((always_inline)) {
+            float t = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) mp[2 * kb + (v >> 3)] = fmaxf(mp[2 * kb + (v >> 3)], sc[kb][v]);
-        float mraw = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
-        mraw = pair_max_halves(mraw);
-        const float mx = mraw == kNegInf ? kNegInf : mraw * c;
-        const float m_new = fmaxf(m, mx);
-        const bool grow = m_new > m + 8.0f;
-        if (wave_any(grow)) {
-            keep_branch();
-            const float alpha = grow ? exp2_fast(m - m_new) : 1.0f;
-            m = grow ? m_new : m;
-            lsum *= alpha;
+                for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+                    for (int e = 0; e < 4; ++e) {
+                        const float p0 = exp2_fast(__builtin_fmaf(sc[kb][8 * cc + 2 * e], c, nm));
+                        const float p1 = exp2_fast(__builtin_fmaf(sc[kb][8 * cc + 2 * e + 1], c, nm));
+                        pk[kb][cc][e] = pack_bf16x2(p0, p1);
+                        t = (kb | cc | e) ? t + (p0 + p1) : p0 + p1;
+                    }
+            return t;
+        };
+        // The reference m only has to bound the exponents: every P must stay
+        // at most 2^8.  Once every row of the wave has a finite m, the tile's
+        // P are formed against it first; a lane sum of at most 2^8 shows that
+        // no P of the lane exceeds it, and the tile is done without a row max.
+        // Otherwise (a row's first visible keys, or scores that grew past
+        // the reference) the row max is taken and m moves to it.
+        bool redo = true;
+        float t = 0.f;
+        if (!wave_any(m == kNegInf)) {
+            t = exp_tile(-m);
+            redo = wave_any(t > 256.0f);
         }
-        const float nm = (m == kNegInf) ? 0.f : -m;
-        // P = 2^(s c - m) -> bf16 pairs; the row sum adds the fp32 values.
+        if (redo) {
+            keep_branch();
+            // Row max of the raw scores (c > 0, so scaling preserves order),
+            // as four independent partial maxima.
+            float mp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc)
+                for (int v = 0; v < 16; ++v) mp[2 * kb + (v >> 3)] = fmaxf(mp[2 * kb + (v >> 3)], sc[kb][v]);
+            float mraw = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+            mraw = pair_max_halves(mraw);
+            const float mx = mraw == kNegInf ? kNegInf : mraw * c;
+            const float m_new = fmaxf(m, mx);
+            const bool grow = m_new > m;
+            if (wave_any(grow)) {
+                const float alpha = grow ? exp2_fast(m - m_new) : 1.0f;
+                m = grow ? m_new : m;
+                lsum *= alpha;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p0 = exp2_fast(__builtin_fmaf(sc[kb][8 * cc + 2 * e], c, nm));
-                    const float p1 = exp2_fast(__builtin_fmaf(sc[kb][8 * cc + 2 * e + 1], c, nm));
-                    pk[kb][cc][e] = pack_bf16x2(p0, p1);
-                    lsum += p0 + p1;
-                }
+                for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+            }
+            t = exp_tile((m == kNegInf) ? 0.f : -m);
+        }
+        lsum += t;
     };
 
     // ---- steps s = 0..n: K(s) in k_s[s & 1], V(s) in v_s[s & 1] ----------
