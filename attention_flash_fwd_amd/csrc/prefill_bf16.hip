@@ -243,20 +243,26 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int n_items)
         const int r = slot / T::cpr, p = slot % T::cpr;
         src_off[i] = (uint32_t)(PAGED ? r - kBS * (wave >> 1) : r) * row_bytes + (uint32_t)T::swz(r, p) * 16u;
     }
-    auto load_slot = [&](__amdgpu_buffer_rsrc_t r, uint16_t *dst) __attribute__((always_inline)) {
+    // Loads of one K or V tile; off (wave-uniform) is added to every lane's
+    // source offset.
+    auto load_slot = [&](__amdgpu_buffer_rsrc_t r, uint16_t *dst, uint32_t off) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < T::lpw; ++i) buffer_load_lds16(r, dst + (wave * T::lpw + i) * 64 * 8, src_off[i]);
+        for (int i = 0; i < T::lpw; ++i) buffer_load_lds16(r, dst + (wave * T::lpw + i) * 64 * 8, src_off[i] + off);
     };
 
-    // Contiguous keys: descriptors over [first key of tile j, end of the keys).
+    // Contiguous keys: one descriptor each for K and V over this (batch, KV
+    // head)'s keys, made once per item; tile j starts tile_off(j) bytes in.
+    // Rows past the keys, and tiles past the item's last one (offset span),
+    // read as zero.
     const size_t head_off = PAGED ? 0 : ((size_t)b * a.Sk * a.Hkv + hk) * D;      // elements
     const char *kbase = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k) + head_off);
     const char *vbase = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.v) + head_off);
     const uint32_t span = Sk > 0 ? (uint32_t)(((size_t)(Sk - 1) * a.Hkv * D + D) * 2) : 0u;
-    auto rsrc_tile = [&](const char *base, int j) __attribute__((always_inline)) {
-        const uint32_t start = (uint32_t)(j * kBC) * row_bytes;
-        const uint32_t left = (j < n && span > start) ? span - start : 0u;
-        return make_rsrc(base + start, left);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, span), rv = make_rsrc(vbase, span);
+    const int n_u = (int)uniform_u32((uint32_t)n);
+    const uint32_t span_u = uniform_u32(span), row_bytes_u = uniform_u32(row_bytes);
+    auto tile_off = [&](int j) __attribute__((always_inline)) {
+        return j < n_u ? (uint32_t)(j * kBC) * row_bytes_u : span_u;
     };
 
     // Paged keys: wave w's cache block of tile t is 4 t + w / 2; its physical
@@ -491,17 +497,17 @@ prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int n_items)
     // barrier); they land by step s's closing barrier.
     auto issue = [&](int s, uint16_t *k_ld, uint16_t *v_ld) __attribute__((always_inline)) {
         if constexpr (PAGED) {
-            load_slot(desc_k, k_ld);
-            load_slot(desc_v, v_ld);
+            load_slot(desc_k, k_ld, 0u);
+            load_slot(desc_v, v_ld, 0u);
         } else {
-            load_slot(rsrc_tile(kbase, s + 1), k_ld);
-            load_slot(rsrc_tile(vbase, s), v_ld);
+            load_slot(rk, k_ld, tile_off(s + 1));
+            load_slot(rv, v_ld, tile_off(s));
         }
     };
     if constexpr (PAGED)
-        load_slot(rsrc_block(a.k, 0, lookup(0)), k_s0);
+        load_slot(rsrc_block(a.k, 0, lookup(0)), k_s0, 0u);
     else
-        load_slot(rsrc_tile(kbase, 0), k_s0);
+        load_slot(rk, k_s0, tile_off(0));
     __syncthreads();
     if (n > 0) {
         auto body0 = [&](int s, const uint16_t *ks, const uint16_t *vs, uint16_t *k_ld, uint16_t *v_ld)
