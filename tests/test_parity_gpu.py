@@ -216,6 +216,32 @@ def test_prefill_negative_scale_and_large_logits(afa, dtype, scale_mul, q_mul):
         check_lse(lse, lse_ref, F32_MAX_ABS)
 
 
+@pytest.mark.parametrize("causal,D,profile", [
+    (True, 128, "ramp"),        # key norms grow 1x -> 6x along the keys: the reference moves often
+    (False, 128, "ramp"),
+    (True, 64, "bump"),         # one 3x tile in the middle, then back to 1x
+    (False, 128, "bump"),
+])
+def test_prefill_scores_growing_along_keys(afa, causal, D, profile):
+    """Scores that grow from tile to tile, so that the exponent reference
+    has to move after a row's first tile: by a little (where the tile sums
+    exceed the bound although the growth is small) or by a lot."""
+    say(f"case prefill growing scores causal{causal} D{D} {profile}")
+    B, S, Hq, Hkv = 1, 700, 4, 2
+    q, k, v = gen_prefill(B, S, S, Hq, Hkv, D, torch.bfloat16, 53)
+    j = torch.arange(S, dtype=torch.float32)
+    if profile == "ramp":
+        r = 1.0 + 5.0 * j / (S - 1)
+    else:
+        r = torch.where((j >= 320) & (j < 384), torch.tensor(3.0), torch.tensor(1.0))
+    k = (k.float() * r[None, :, None, None]).to(torch.bfloat16)
+    scale = 1 / math.sqrt(D)
+    o, lse = run_prefill(afa, q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.attention(to_np(q), to_np(k), to_np(v), causal, scale)
+    check_o(o, o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(lse, lse_ref, BF16_LSE_ABS)
+
+
 def test_decode_negative_scale_and_large_logits(afa):
     say("case decode scale < 0 and q x 16")
     inp = gen_decode([700, 33], 8, 2, 128, seed=41)
