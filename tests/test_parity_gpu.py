@@ -509,6 +509,36 @@ def test_prefill_paged_small(afa, ctx, Sq, Hq, Hkv, D, causal):
     check_lse(to_np(lse), l_ref, BF16_LSE_ABS)
 
 
+def test_prefill_paged_scores_growing_along_keys(afa):
+    """The paged kernel's softmax under scores that grow along the keys (key
+    norms ramped 1x -> 6x), so the exponent reference moves after a row's
+    first tile."""
+    ctx, Sq, Hq, Hkv, D = [700, 333], 300, 8, 2, 128
+    say(f"case prefill_paged growing scores ctx{ctx} Sq{Sq}")
+    inp, q = gen_paged_prefill(ctx, Sq, Hq, Hkv, D, seed=61, spare_blocks=3)
+    bs = inp.k_cache.shape[1]
+    tbl = inp.block_table.cpu()
+    k_cache = inp.k_cache.clone()
+    ks, vs = [], []
+    for b, n in enumerate(ctx):
+        r = 1.0 + 5.0 * torch.arange(n, dtype=torch.float32) / (n - 1)
+        kb, vb = inp.logical_kv(b, device="cpu")
+        kb = (kb.float() * r[:, None, None]).to(torch.bfloat16)
+        for lb in range((n + bs - 1) // bs):
+            lo, hi = lb * bs, min(n, (lb + 1) * bs)
+            k_cache[int(tbl[b, lb]), :hi - lo] = kb[lo:hi].to(k_cache.device)
+        ks.append(kb)
+        vs.append(vb)
+    scale = 1 / math.sqrt(D)
+    o, lse = afa.prefill_paged(q, k_cache, inp.v_cache, inp.block_table, inp.ctx_lens, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    qn = to_np(q)
+    ref = [oracle.attention(qn[b:b + 1], ks[b].float().numpy()[None], vs[b].float().numpy()[None], True, scale)
+           for b in range(len(ctx))]
+    check_o(to_np(o), np.concatenate([r_[0] for r_ in ref]), BF16_MAX_ABS, BF16_MEAN_ABS)
+    check_lse(to_np(lse), np.concatenate([r_[1] for r_ in ref]), BF16_LSE_ABS)
+
+
 def test_prefill_paged_equals_contiguous_and_permutation(afa):
     # With the whole sequence as the chunk, paged prefill is the contiguous
     # prefill on the same keys: same kernel arithmetic, bit-identical output.
