@@ -216,18 +216,20 @@ def test_prefill_negative_scale_and_large_logits(afa, dtype, scale_mul, q_mul):
         check_lse(lse, lse_ref, F32_MAX_ABS)
 
 
-@pytest.mark.parametrize("causal,D,profile", [
-    (True, 128, "ramp"),        # key norms grow 1x -> 6x along the keys: the reference moves often
-    (False, 128, "ramp"),
-    (True, 64, "bump"),         # one 3x tile in the middle, then back to 1x
-    (False, 128, "bump"),
+@pytest.mark.parametrize("causal,D,profile,Hq,Hkv", [
+    (True, 128, "ramp", 4, 2),      # key norms grow 1x -> 6x along the keys: the reference moves often
+    (False, 128, "ramp", 4, 2),
+    (True, 64, "bump", 4, 2),       # one 3x tile in the middle, then back to 1x
+    (False, 128, "bump", 4, 2),
+    (True, 128, "ramp", 8, 2),      # four query heads per work item
+    (True, 128, "bump", 3, 1),      # odd group: one query head per work item
 ])
-def test_prefill_scores_growing_along_keys(afa, causal, D, profile):
+def test_prefill_scores_growing_along_keys(afa, causal, D, profile, Hq, Hkv):
     """Scores that grow from tile to tile, so that the exponent reference
     has to move after a row's first tile: by a little (where the tile sums
     exceed the bound although the growth is small) or by a lot."""
-    say(f"case prefill growing scores causal{causal} D{D} {profile}")
-    B, S, Hq, Hkv = 1, 700, 4, 2
+    say(f"case prefill growing scores causal{causal} D{D} {profile} Hq{Hq} Hkv{Hkv}")
+    B, S = 1, 700
     q, k, v = gen_prefill(B, S, S, Hq, Hkv, D, torch.bfloat16, 53)
     j = torch.arange(S, dtype=torch.float32)
     if profile == "ramp":
